@@ -1,0 +1,108 @@
+"""Seeded synthetic q/k/v generators for the hybrid attention workloads.
+
+This module holds no attention arithmetic: it only draws random tensors with
+the shapes and value distributions of the workloads, so that the GPU library
+and the CPU oracle can be handed the very same values.
+
+Workload shapes follow the video geometry of "ReHyAt: Recurrent Hybrid
+Attention for Video Diffusion Transformers" (§4.1 and §5.2): a 5 s, 81-frame
+480x832 clip is a 21 x 30 x 52 latent (21 frames of 1560 tokens), the ablation
+resolution 320x480 is 21 x 20 x 30.  Heads H = 12 and head_dim 128 are the
+Wan2.1-1.3B attention shape.  Values are i.i.d. N(0, 1) for queries and values,
+N(0, 1)/sqrt(head_dim) for keys (the softmax scale folded into the keys), drawn
+in float32 with numpy's PCG64 and rounded to bfloat16 (round-to-nearest-even)
+by torch where the workload is bf16.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed_id: int            # seeds are default_rng(1000*seed_id + s), s = 0/1/2/3 for q/k/v/outliers
+    B: int
+    H: int
+    head_dim: int
+    frames: int
+    tokens_per_frame: int
+    chunk_frames: int
+    overlap_frames: int
+    dtype: str              # "f32" or "bf16"
+    key_scale: float = 1.0
+    outlier_frac: float = 0.0   # fraction of key rows replaced by N(0, outlier_std^2), not scaled
+    outlier_std: float = 0.0
+
+    @property
+    def N(self) -> int:
+        return self.frames * self.tokens_per_frame
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.N
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+_S128 = 1.0 / math.sqrt(128.0)
+
+WORKLOADS = {
+    # tiny fp32 check: 4 frames of 8x8 tokens
+    "tiny_f4x8x8": Workload("tiny_f4x8x8", 1, 1, 2, 16, 4, 64, 1, 1, "f32"),
+    # Wan2.1-1.3B attention at 480x832, 81 frames -> latent 21 x 30 x 52
+    "wan_21x30x52": Workload("wan_21x30x52", 2, 1, 12, 128, 21, 1560, 3, 1, "bf16", _S128),
+    # same with the CFG cond/uncond pair as B = 2 (chunk_frames swept by the caller)
+    "wan_cfg_21x30x52": Workload("wan_cfg_21x30x52", 3, 2, 12, 128, 21, 1560, 3, 1, "bf16", _S128),
+    # long video, 105 latent frames of 1560 tokens, processed chunk by chunk
+    "wan_long_105x30x52": Workload("wan_long_105x30x52", 4, 1, 12, 128, 105, 1560, 3, 1, "bf16", _S128),
+    # higher resolution 21 x 45 x 80 with 1% outlier key rows ~ N(0, 16)
+    "wan_outlier_21x45x80": Workload("wan_outlier_21x45x80", 5, 1, 12, 128, 21, 3600, 3, 1, "bf16",
+                                     _S128, 0.01, 4.0),
+}
+
+
+def _draw(seed: int, shape, scale: float = 1.0) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return x
+
+
+def make_qkv(w: Workload, device="cpu"):
+    """(q, k, v) torch tensors [B, H, N, d] in the workload's dtype."""
+    shape = (w.B, w.H, w.N, w.head_dim)
+    base = 1000 * w.seed_id
+    q = _draw(base + 0, shape)
+    k = _draw(base + 1, shape, w.key_scale)
+    v = _draw(base + 2, shape)
+    if w.outlier_frac > 0.0:
+        rng = np.random.Generator(np.random.PCG64(base + 3))
+        rows = rng.random((w.B, w.H, w.N)) < w.outlier_frac
+        vals = rng.standard_normal((int(rows.sum()), w.head_dim), dtype=np.float32)
+        k[rows] = vals * np.float32(w.outlier_std)
+    out = []
+    for x in (q, k, v):
+        t = torch.from_numpy(x).to(w.torch_dtype)
+        out.append(t.to(device) if device != "cpu" else t)
+    return tuple(out)
+
+
+def custom(B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
+           dtype="bf16", seed_id=100, key_scale=None) -> Workload:
+    """An ad-hoc workload (tests: ragged tails, odd geometries)."""
+    if key_scale is None:
+        key_scale = 1.0 / math.sqrt(head_dim) if dtype == "bf16" else 1.0
+    return Workload(f"custom_{B}x{H}x{frames}x{tokens_per_frame}x{head_dim}", seed_id, B, H,
+                    head_dim, frames, tokens_per_frame, chunk_frames, overlap_frames, dtype,
+                    key_scale)

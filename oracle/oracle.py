@@ -1,0 +1,254 @@
+"""Plain fp64 CPU oracle for the ReHyAt hybrid attention forward.
+
+TEST INFRASTRUCTURE ONLY.  This module is the correctness reference the GPU
+library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code with the
+GPU library and never imports it.
+
+Source throughout: "ReHyAt: Recurrent Hybrid Attention for Video Diffusion
+Transformers" (Ghafoorian & Habibian, arXiv 2601.04342), §3.1-§3.3.
+
+Three independent forms of the same computation live here:
+
+* :func:`definition` -- the fp64 C code in ``rehyat_oracle.c``: per query, an
+  explicit walk over every key that classifies it as softmax / linear / ignored
+  by the §3.3 partition, literal exponentials, joint normalisation (§3.2).
+* :func:`brute_force` -- a numpy matrix form for tiny inputs: 0/1 masks built
+  from the §3.3 set definitions written in token units, ``W = exp(QK^T)*M_S +
+  (phi(Q) phi(K)^T)*M_L``, ``Y = W V / rowsum(W)``.
+* :class:`RecurrentState` / :func:`recurrent` -- the chunk-wise RNN form the
+  paper derives (§3.3 and the abstract's "chunk-wise recurrent reformulation and
+  constant memory usage"): chunks in order, carrying the linear sums (S, z) of
+  §3.1 plus the keys/values of the last T_o frames (the next chunk's overlap).
+
+Readings where the text is silent are listed in ``rehyat_oracle.c``'s header;
+they apply here too.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+PHI_NONE, PHI_ELU1, PHI_POLY2 = 0, 1, 2
+PHI_NAMES = {"none": PHI_NONE, "elu1": PHI_ELU1, "poly2": PHI_POLY2}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rehyat_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "librehyat_oracle.so")
+_lib = None
+
+
+def phi_kind(phi) -> int:
+    if isinstance(phi, str):
+        return PHI_NAMES[phi.lower()]
+    return int(phi)
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (-O2, OpenMP, IEEE arithmetic: no fast-math)."""
+    stale = (not os.path.exists(_LIB_PATH)
+             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+    if force or stale:
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                        "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lp = ctypes.POINTER(ctypes.c_longlong)
+        lib.rehyat_oracle_fwd.restype = ctypes.c_int
+        lib.rehyat_oracle_fwd.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 8 + [
+            ctypes.c_double, ctypes.c_int, lp, ctypes.c_longlong, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.rehyat_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return _load().rehyat_oracle_max_threads()
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def definition(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, phi="elu1",
+               scale=1.0, causal=True, rows=None, partials=False, nthreads=0):
+    """Definition form (C, fp64).  q, k, v: [B, H, N, d], N = frames * tokens_per_frame.
+
+    ``rows``: optional 1-D array of query indices (same for every (b, h)); the
+    outputs then have that many rows.  Returns ``y`` or ``(y, parts)`` where
+    ``parts`` has m, nt (= sum exp(s - m) over the softmax set), oS, oL, nL.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    assert N == frames * tokens_per_frame
+    kind = phi_kind(phi)
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R = rows.shape[0]
+    else:
+        R = N
+    y = np.empty((B, H, R, d), dtype=np.float64)
+    parts = None
+    if partials:
+        parts = {"m": np.empty((B, H, R)), "nt": np.empty((B, H, R)),
+                 "oS": np.empty((B, H, R, d)), "oL": np.empty((B, H, R, d)),
+                 "nL": np.empty((B, H, R))}
+    lib = _load()
+    rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong)) if rows is not None else None
+    st = lib.rehyat_oracle_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(y), B, H, frames, tokens_per_frame, d,
+        chunk_frames, overlap_frames, kind, float(scale), 1 if causal else 0,
+        rows_p, R,
+        _ptr(parts["m"]) if parts else None, _ptr(parts["nt"]) if parts else None,
+        _ptr(parts["oS"]) if parts else None, _ptr(parts["oL"]) if parts else None,
+        _ptr(parts["nL"]) if parts else None, int(nthreads))
+    if st == 1:
+        raise ValueError("oracle: invalid arguments")
+    if st == 2:
+        raise FloatingPointError("oracle: a sum is not finite (|score| too large for exp in fp64)")
+    return (y, parts) if partials else y
+
+
+# ---------------------------------------------------------------------------
+# numpy forms
+# ---------------------------------------------------------------------------
+
+def feature_map(x: np.ndarray, phi) -> np.ndarray:
+    """phi of §3.1/§3.2 on the last axis.  ELU1: 1 + elu(x) (alpha 1); POLY2:
+    [1 + elu(x), x^2] (D' = 2d); NONE: an empty feature vector."""
+    kind = phi_kind(phi)
+    x = np.asarray(x, dtype=np.float64)
+    if kind == PHI_NONE:
+        return np.zeros(x.shape[:-1] + (0,))
+    e = np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+    if kind == PHI_ELU1:
+        return e
+    if kind == PHI_POLY2:
+        return np.concatenate([e, x * x], axis=-1)
+    raise ValueError(phi)
+
+
+def masks(N, tokens_per_frame, chunk_frames, overlap_frames, causal=True):
+    """0/1 key masks (M_S, M_L), [N, N], from the §3.3 sets written in tokens:
+    N' = T_c HW, query i is in chunk t = floor(i / N'), T^S_t = {j : max(tN' -
+    T_o HW, 0) <= j < (t+1)N'}, T^L_t = {j : j < max(tN' - T_o HW, 0)} (causal)
+    or the complement of T^S_t (non-causal, §3.2)."""
+    HW = tokens_per_frame
+    n_chunk = chunk_frames * HW
+    i = np.arange(N)
+    t = i // n_chunk
+    lo = np.maximum(t * n_chunk - overlap_frames * HW, 0)
+    hi = (t + 1) * n_chunk
+    j = np.arange(N)[None, :]
+    m_s = (j >= lo[:, None]) & (j < hi[:, None])
+    m_l = (j < lo[:, None]) if causal else ~m_s
+    return m_s, m_l
+
+
+def brute_force(q, k, v, tokens_per_frame, chunk_frames, overlap_frames, phi="elu1",
+                scale=1.0, causal=True):
+    """Matrix form for tiny inputs: Y = (exp(s QK^T) M_S + phi(Q)phi(K)^T M_L) V / rowsum."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N = q.shape[-2]
+    m_s, m_l = masks(N, tokens_per_frame, chunk_frames, overlap_frames, causal)
+    s = scale * (q @ np.swapaxes(k, -1, -2))
+    w = np.where(m_s, np.exp(np.where(m_s, s, 0.0)), 0.0)
+    if phi_kind(phi) != PHI_NONE:
+        w = w + np.where(m_l, feature_map(q, phi) @ np.swapaxes(feature_map(k, phi), -1, -2), 0.0)
+    return (w @ v) / w.sum(axis=-1, keepdims=True)
+
+
+class RecurrentState:
+    """Chunk-wise RNN form (fp64): one chunk of T_c frames per :meth:`step`.
+
+    Carried between steps: S = sum phi(k) v^T and z = sum phi(k) over every key
+    that has left the softmax window (the cached sums of §3.1), the keys and
+    values of the last min(T_o, frames so far) frames (the next chunk's overlap,
+    §3.3), and the number of frames processed.  Its size does not depend on how
+    many frames have been processed.
+    """
+
+    def __init__(self, B, H, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
+                 phi="elu1", scale=1.0):
+        self.HW, self.d = tokens_per_frame, head_dim
+        self.Tc, self.To = chunk_frames, overlap_frames
+        self.phi, self.scale = phi_kind(phi), scale
+        Dp = feature_map(np.zeros((1, head_dim)), phi).shape[-1]
+        self.S = np.zeros((B, H, Dp, head_dim))
+        self.z = np.zeros((B, H, Dp))
+        self.k_prev = np.zeros((B, H, 0, head_dim))
+        self.v_prev = np.zeros((B, H, 0, head_dim))
+        self.frames_done = 0
+
+    def carried_nbytes(self) -> int:
+        """Bytes carried to the next step, at their maximum (T_o frames of K/V)."""
+        B, H = self.S.shape[:2]
+        return (self.S.nbytes + self.z.nbytes
+                + 2 * B * H * self.To * self.HW * self.d * 8)
+
+    def step(self, qc, kc, vc):
+        """Attend one chunk; q/k/v chunks are [B, H, n_frames*HW, d]."""
+        qc, kc, vc = _f64(qc), _f64(kc), _f64(vc)
+        nf = qc.shape[-2] // self.HW
+        assert qc.shape[-2] == nf * self.HW and nf >= 1
+        # window = overlap frames carried from earlier chunks + this chunk
+        kw = np.concatenate([self.k_prev, kc], axis=-2)
+        vw = np.concatenate([self.v_prev, vc], axis=-2)
+        e = np.exp(self.scale * (qc @ np.swapaxes(kw, -1, -2)))     # softmax set
+        a_s = e @ vw
+        n_s = e.sum(axis=-1)
+        fq = feature_map(qc, self.phi)                               # linear set
+        a_l = fq @ self.S
+        n_l = (fq * self.z[:, :, None, :]).sum(axis=-1)
+        y = (a_s + a_l) / (n_s + n_l)[..., None]                     # joint normalisation
+        # the next window starts T_o frames before the next chunk: keep the last
+        # min(T_o, frames so far) frames, fold the rest of the window into (S, z)
+        self.frames_done += nf
+        keep = min(self.To, self.frames_done) * self.HW
+        n_ev = kw.shape[-2] - keep
+        if n_ev > 0:
+            fk = feature_map(kw[:, :, :n_ev], self.phi)
+            self.S = self.S + np.swapaxes(fk, -1, -2) @ vw[:, :, :n_ev]
+            self.z = self.z + fk.sum(axis=-2)
+        self.k_prev = kw[:, :, n_ev:]
+        self.v_prev = vw[:, :, n_ev:]
+        return y
+
+
+def recurrent(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, phi="elu1",
+              scale=1.0, return_state_sizes=False):
+    """Whole clip through :class:`RecurrentState`, chunk by chunk."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    HW = tokens_per_frame
+    assert N == frames * HW
+    st = RecurrentState(B, H, HW, d, chunk_frames, overlap_frames, phi, scale)
+    out = np.empty_like(q)
+    sizes = []
+    for f0 in range(0, frames, chunk_frames):
+        f1 = min(f0 + chunk_frames, frames)
+        sl = slice(f0 * HW, f1 * HW)
+        out[:, :, sl] = st.step(q[:, :, sl], k[:, :, sl], v[:, :, sl])
+        sizes.append(st.S.nbytes + st.z.nbytes + st.k_prev.nbytes + st.v_prev.nbytes)
+    return (out, sizes, st) if return_state_sizes else out

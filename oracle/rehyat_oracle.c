@@ -1,0 +1,194 @@
+/*
+ * rehyat_oracle.c -- plain fp64 CPU oracle for the ReHyAt hybrid attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
+ * GPU library is checked against.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it; the library never does.  It
+ * shares no code, header or table with the GPU path.
+ *
+ * Source: "ReHyAt: Recurrent Hybrid Attention for Video Diffusion Transformers"
+ * (Ghafoorian & Habibian, arXiv 2601.04342).
+ *   - §3.1, second display equation: generic similarity attention
+ *       y_i = sum_j sim(q_i,k_j) v_j / sum_j sim(q_i,k_j).
+ *   - §3.1, third equation and the paragraph after it: linear attention with a
+ *     non-negative feature map, phi(x) = 1 + elu(x) (Katharopoulos et al.).
+ *   - §3.2, first equation: the hybrid output is the sum of the softmax and the
+ *     linear numerators over the sum of the two normalisers (joint normalisation).
+ *   - §3.3, equation: the recurrent (causal) partition of the keys for chunk t,
+ *       softmax set  T^S_t = { j : max(tN' - T_o HW, 0) <= j < (t+1)N' }
+ *       linear set   T^L_t = { j : j < max(tN' - T_o HW, 0) }
+ *     with N' = T_c * HW tokens per chunk (the reading forced by the T_o HW term).
+ *   - §3.2, second/third equations: the non-causal variant, where the linear set
+ *     is every key outside the softmax set (causal = 0 below).
+ *
+ * Readings where the text is silent (all documented with the design notes):
+ *   - softmax similarity is exp(scale * q.k); scale is an argument (1 in the
+ *     library's contract: callers fold 1/sqrt(d) into the keys);
+ *   - frame-major token order, frames numbered from 0, chunks start at frame 0,
+ *     the last chunk may be partial;
+ *   - the overlap is the T_o frames *preceding* a chunk, clipped at frame 0;
+ *   - same phi for queries and keys; ELU1 = elu(x)+1 (alpha = 1), POLY2 =
+ *     [elu(x)+1 ; x*x] (a parameter-free degree-2 instance of the polynomial
+ *     feature map of §3.2), NONE = no linear branch.
+ *
+ * The exponential is the literal one, with no max subtraction: every key weight
+ * is exactly exp(s).  That is finite in fp64 while s < 709; the function reports
+ * an error if any sum is not finite.
+ *
+ * Per query the code walks *every* key j in [0, N) and classifies it as softmax,
+ * linear or ignored.  No state is cached across queries; the only hoisting is
+ * that phi is applied once to every key row (the same values the definition
+ * uses).  OpenMP parallelises over (batch, head, query); each query's sums are
+ * accumulated sequentially in key order.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+enum { ORACLE_PHI_NONE = 0, ORACLE_PHI_ELU1 = 1, ORACLE_PHI_POLY2 = 2 };
+
+/* elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise (§3.1). */
+static double elu1(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* Feature dimension D' of phi for head dimension d. */
+int rehyat_oracle_feature_dim(int phi_kind, int d) {
+    switch (phi_kind) {
+    case ORACLE_PHI_NONE: return 0;
+    case ORACLE_PHI_ELU1: return d;
+    case ORACLE_PHI_POLY2: return 2 * d;
+    default: return -1;
+    }
+}
+
+/* phi(x) for one row x[0..d) into out[0..D'). */
+static void feature_map(int phi_kind, const double* x, int d, double* out) {
+    if (phi_kind == ORACLE_PHI_ELU1) {
+        for (int c = 0; c < d; ++c) out[c] = elu1(x[c]);
+    } else if (phi_kind == ORACLE_PHI_POLY2) {
+        for (int c = 0; c < d; ++c) out[c] = elu1(x[c]);
+        for (int c = 0; c < d; ++c) out[d + c] = x[c] * x[c];
+    }
+}
+
+/*
+ * Hybrid attention forward, definition form.
+ *
+ *   q, k, v : [B][H][N][d] fp64, N = F * HW, frame-major.
+ *   rows    : optional list of nrows query indices in [0, N) (the same for every
+ *             (b, h)); NULL means all N queries in order (nrows ignored).
+ *   y       : [B][H][R][d] where R = nrows if rows != NULL, else N.
+ *   part_*  : optional per-query partials, each [B][H][R] except the two
+ *             branch outputs which are [B][H][R][d]; any may be NULL:
+ *               m   = max_{j in T^S} s_ij
+ *               nt  = sum_{j in T^S} exp(s_ij - m)
+ *               oS  = a^S / n^S                  (softmax-branch output)
+ *               oL  = a^L / n^L  (0 if n^L == 0) (linear-branch output)
+ *               nL  = n^L
+ *   causal  : 1 = recurrent partition of §3.3 (keys after the chunk ignored);
+ *             0 = non-causal partition of §3.2 (they join the linear set).
+ *   nthreads: OpenMP threads (<= 0: library default).
+ *
+ * Returns 0 on success, 1 on invalid arguments, 2 if a sum is not finite.
+ */
+int rehyat_oracle_fwd(const double* q, const double* k, const double* v, double* y,
+                      int B, int H, int F, int HW, int d, int Tc, int To, int phi_kind,
+                      double scale, int causal, const long long* rows, long long nrows,
+                      double* part_m, double* part_nt, double* part_oS, double* part_oL,
+                      double* part_nL, int nthreads) {
+    if (!q || !k || !v || !y || B < 1 || H < 1 || F < 1 || HW < 1 || d < 1 || Tc < 1 || To < 0)
+        return 1;
+    const int Dp = rehyat_oracle_feature_dim(phi_kind, d);
+    if (Dp < 0) return 1;
+    const long long N = (long long)F * HW;
+    const long long R = rows ? nrows : N;
+    if (R < 0) return 1;
+    if (rows) {
+        for (long long r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= N) return 1;
+    }
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+
+    /* phi applied once to every key row. */
+    double* phik = NULL;
+    if (Dp > 0) {
+        phik = (double*)malloc(sizeof(double) * (size_t)B * H * N * Dp);
+        if (!phik) return 1;
+#pragma omp parallel for schedule(static)
+        for (long long r = 0; r < (long long)B * H * N; ++r)
+            feature_map(phi_kind, k + r * d, d, phik + r * Dp);
+    }
+
+    int status = 0;
+#pragma omp parallel
+    {
+        double* aS = (double*)malloc(sizeof(double) * d);
+        double* aL = (double*)malloc(sizeof(double) * d);
+        double* phiq = (double*)malloc(sizeof(double) * (Dp > 0 ? Dp : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (long long task = 0; task < (long long)B * H * R; ++task) {
+            const long long bh = task / R, r = task % R;
+            const long long i = rows ? rows[r] : r;
+            const double* qi = q + (bh * N + i) * d;
+            const double* kb = k + bh * N * d;
+            const double* vb = v + bh * N * d;
+            const double* pk = phik ? phik + bh * N * Dp : NULL;
+
+            /* chunk of query i and its softmax window, in token units */
+            const long long f = i / HW;
+            const long long t = f / Tc;
+            long long w0f = t * Tc - To;
+            if (w0f < 0) w0f = 0;
+            long long w1f = (t + 1) * Tc;
+            if (w1f > F) w1f = F;
+            const long long w0 = w0f * HW, w1 = w1f * HW;
+
+            if (Dp > 0) feature_map(phi_kind, qi, d, phiq);
+            for (int c = 0; c < d; ++c) { aS[c] = 0.0; aL[c] = 0.0; }
+            double nS = 0.0, nL = 0.0, m = -INFINITY;
+
+            for (long long j = 0; j < N; ++j) {
+                const double* vj = vb + j * d;
+                if (j >= w0 && j < w1) {                       /* softmax set */
+                    double s = 0.0;
+                    const double* kj = kb + j * d;
+                    for (int c = 0; c < d; ++c) s += qi[c] * kj[c];
+                    s *= scale;
+                    if (s > m) m = s;
+                    const double e = exp(s);
+                    nS += e;
+                    for (int c = 0; c < d; ++c) aS[c] += e * vj[c];
+                } else if (Dp > 0 && (j < w0 || !causal)) {     /* linear set */
+                    double w = 0.0;
+                    const double* pkj = pk + j * Dp;
+                    for (int c = 0; c < Dp; ++c) w += phiq[c] * pkj[c];
+                    nL += w;
+                    for (int c = 0; c < d; ++c) aL[c] += w * vj[c];
+                }                                               /* else ignored */
+            }
+            const double den = nS + nL;
+            if (!isfinite(den) || !(den > 0.0)) {
+#pragma omp atomic write
+                status = 2;
+            }
+            double* yi = y + (bh * R + r) * d;
+            for (int c = 0; c < d; ++c) yi[c] = (aS[c] + aL[c]) / den;
+            if (part_m) part_m[bh * R + r] = m;
+            if (part_nt) part_nt[bh * R + r] = nS * exp(-m);
+            if (part_nL) part_nL[bh * R + r] = nL;
+            if (part_oS)
+                for (int c = 0; c < d; ++c) part_oS[(bh * R + r) * d + c] = aS[c] / nS;
+            if (part_oL)
+                for (int c = 0; c < d; ++c)
+                    part_oL[(bh * R + r) * d + c] = nL > 0.0 ? aL[c] / nL : 0.0;
+        }
+        free(aS);
+        free(aL);
+        free(phiq);
+    }
+    free(phik);
+    return status;
+}
+
+/* Number of OpenMP threads a parallel region would use. */
+int rehyat_oracle_max_threads(void) { return omp_get_max_threads(); }
