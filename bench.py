@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReHyAt hybrid attention forward on one MI355X.
+
+One step = one whole-clip forward (block-state pass, cross-chunk scan, local
+softmax + fused combine) over the Wan2.1-1.3B attention shape: B=1, H=12,
+head_dim=128, 21 latent frames of 30x52 = 1560 tokens (a 5 s 480x832 clip),
+T_c = 3, T_o = 1, elu+1 features, bf16 in/out with fp32 accumulation, q/k/v
+resident in HBM before timing starts.
+
+Prints ONE JSON line: tokens/s of the whole step, the local-softmax kernel
+against the bf16 MFMA roofline (its duration taken from HIP events recorded
+around that kernel on its own stream during the timed steps), the state pass
+against the HBM roofline, the dense bidirectional softmax companion at the same
+shape, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# HBM bytes per dispatch of the local-softmax kernel from rocprofv3 FETCH_SIZE +
+# WRITE_SIZE, scaled by the copy-kernel calibration; None until measured for the
+# current kernel.
+LOCAL_KERNEL_TRAFFIC_BYTES = None
+
+
+class Hip:
+    """Minimal HIP event API over ctypes (events on an arbitrary stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def geometry_counts(w, Tc, To, phi_dim):
+    """Algorithmic work of one forward (ReHyAt §3.3 partition).
+
+    softmax FLOPs = 4 d sum_t |Q_t| |W_t| B H (QK^T and PV), exps = sum |Q_t||W_t| B H,
+    state-pass bytes = K and V rows of every delta block read once (bf16) plus the
+    fp32 block sums written once and read once by the scan."""
+    F, HW, d = w.frames, w.tokens_per_frame, w.head_dim
+    C = (F + Tc - 1) // Tc
+    pairs = 0
+    for t in range(C):
+        f0, f1 = t * Tc, min((t + 1) * Tc, F)
+        w0 = max(f0 - To, 0)
+        pairs += (f1 - f0) * HW * (f1 - w0) * HW
+    BH = w.B * w.H
+    flops = 4.0 * d * pairs * BH
+    lin_rows = max((C - 1) * Tc - To, 0) * HW if phi_dim > 0 else 0
+    E = d * phi_dim + phi_dim
+    state_bytes = 2.0 * BH * lin_rows * d * 2 + 3.0 * (C - 1) * BH * E * 4 if phi_dim > 0 else 0.0
+    return {"softmax_flops": flops, "exps": float(pairs * BH), "state_bytes": state_bytes,
+            "chunks": C}
+
+
+def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=True):
+    import torch
+    for _ in range(warmup):
+        rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out)
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(4)] for _ in range(steps)] if profile else None
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if profile:
+            rh.set_profile_events(evs[i])
+        rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if profile:
+        rh.set_profile_events(None)
+    res = {"ms_per_step": (t1 - t0) * 1000.0 / steps}
+    if profile:
+        st = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+        sc = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+        lo = [hip.elapsed_ms(e[2], e[3]) for e in evs]
+        res.update(state_ms=sum(st) / steps, scan_ms=sum(sc) / steps, local_ms=sum(lo) / steps)
+        for e in evs:
+            for x in e:
+                hip.destroy(x)
+    return res
+
+
+def cpu_baseline(w, q, k, v, Tc, To, phi, target_s=15.0):
+    """fp64 oracle (definition form) on a bounded, chunk-stratified sample of query rows."""
+    import numpy as np
+    from oracle import oracle as O
+    q64, k64, v64 = (x.double().numpy() for x in (q, k, v))
+    N = w.N
+    rng = np.random.default_rng(12345)
+
+    def rows_for(n):
+        return np.sort(rng.choice(N, size=n, replace=False)).astype(np.int64)
+
+    n = 32
+    t0 = time.perf_counter()
+    O.definition(q64, k64, v64, w.frames, w.tokens_per_frame, Tc, To, phi, rows=rows_for(n))
+    dt = time.perf_counter() - t0
+    n2 = int(max(32, min(N, n * target_s / max(dt, 1e-3))))
+    rows = rows_for(n2)
+    t0 = time.perf_counter()
+    O.definition(q64, k64, v64, w.frames, w.tokens_per_frame, Tc, To, phi, rows=rows)
+    dt = time.perf_counter() - t0
+    tokens = w.B * n2
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": O.max_threads(), "kind": "oracle",
+            "sample": f"{n2} random query rows of {N} per (b,h), all {w.B * w.H} heads, fp64 "
+                      f"definition form, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan_21x30x52")
+    ap.add_argument("--phi", default="elu1")
+    ap.add_argument("--chunk-frames", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (the hot path is single-GPU; "
+              "multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_video_rehyat_amd as rh
+    from linear_attention_video_rehyat_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    Tc = args.chunk_frames or w.chunk_frames
+    To = w.overlap_frames
+    phi = args.phi
+    phi_dim = {"none": 0, "elu1": w.head_dim, "poly2": 2 * w.head_dim}[phi]
+    hip = Hip()
+
+    q, k, v = inputs.make_qkv(w)
+    qg, kg, vg = (x.to("cuda") for x in (q, k, v))
+    out = torch.empty_like(qg)
+    torch.cuda.synchronize()
+
+    main_t = time_steps(rh, hip, qg, kg, vg, out, w, Tc, To, phi, args.steps, args.warmup)
+    cnt = geometry_counts(w, Tc, To, phi_dim)
+    value = w.tokens / (main_t["ms_per_step"] / 1000.0)
+    local_tflops = cnt["softmax_flops"] / (main_t["local_ms"] / 1000.0) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(local_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(local_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": LOCAL_KERNEL_TRAFFIC_BYTES, "kernel": "local_bf16_kernel",
+                "ms": round(main_t["local_ms"], 4),
+                "algorithmic_flops": cnt["softmax_flops"]}
+    state = None
+    if phi_dim > 0:
+        st_ms = main_t["state_ms"] + main_t["scan_ms"]
+        gbs = cnt["state_bytes"] / (st_ms / 1000.0) / 1e9
+        state = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(gbs / PEAK_HBM_GBS, 4), "state_kernel_ms": round(main_t["state_ms"], 4),
+                 "scan_ms": round(main_t["scan_ms"], 4), "algorithmic_bytes": cnt["state_bytes"]}
+
+    dense = None
+    if not args.no_dense:
+        d_t = time_steps(rh, hip, qg, kg, vg, out, w, w.frames, 0, "none", max(3, args.steps // 4), 1)
+        dc = geometry_counts(w, w.frames, 0, 0)
+        dense = {"tokens_per_s": round(w.tokens / (d_t["ms_per_step"] / 1000.0), 1),
+                 "ms_per_step": round(d_t["ms_per_step"], 4),
+                 "tflops": round(dc["softmax_flops"] / (d_t["local_ms"] / 1000.0) / 1e12, 2),
+                 "hybrid_speedup": round(d_t["ms_per_step"] / main_t["ms_per_step"], 3),
+                 "flop_ratio": round(dc["softmax_flops"] / cnt["softmax_flops"], 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, Tc, To, phi, args.cpu_seconds)
+
+    line = {
+        "metric": "hybrid-attn fwd tokens/s at Wan2.1-1.3B shape; % of MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(main_t["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/v, N(0,1)/sqrt(128) k)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "head_dim": w.head_dim,
+                   "frames": w.frames, "tokens_per_frame": w.tokens_per_frame,
+                   "chunk_frames": Tc, "overlap_frames": To, "feature_map": phi,
+                   "tokens_per_step": w.tokens},
+        "roofline": roofline,
+        "state_pass": state,
+        "dense_softmax": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * rehyat.h -- C ABI of librehyat, the ReHyAt recurrent hybrid attention forward
+ * pass for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "ReHyAt: Recurrent Hybrid Attention for Video Diffusion Transformers"
+ * (Ghafoorian & Habibian, arXiv 2601.04342).  For a query token i of temporal
+ * chunk t (T_c frames of HW tokens each, frame-major token order):
+ *
+ *   softmax set  T^S_t = { j : max(t T_c - T_o, 0) HW <= j < min((t+1) T_c, F) HW }
+ *   linear set   T^L_t = { j : j < max(t T_c - T_o, 0) HW }           (§3.3 equation)
+ *   keys after the chunk are ignored (the causal, recurrent partition);
+ *
+ *   a^S = sum_{T^S} exp(q.k) v      n^S = sum_{T^S} exp(q.k)
+ *   a^L = sum_{T^L} (phi(q).phi(k)) v   n^L = sum_{T^L} phi(q).phi(k)  (§3.1)
+ *   y   = (a^S + a^L) / (n^S + n^L)                          (§3.2, first equation)
+ *
+ * The linear sums over T^L_t are carried from chunk to chunk as the state
+ * (S = sum phi(k) v^T, z = sum phi(k)) of the chunk-wise RNN form (§3.3; the
+ * abstract's "chunk-wise recurrent reformulation and constant memory usage").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device pointers to contiguous [B][H][N][head_dim] arrays,
+ *     N = frames * tokens_per_frame, tokens frame-major.  The caller owns them.
+ *   - The softmax similarity is exp(q.k) with no extra scale: callers fold the
+ *     usual 1/sqrt(head_dim) into k (or q).
+ *   - bf16 entry points: bf16 in and out, fp32 accumulation and fp32 state.
+ *     _f32 entry points: fp32 in and out.
+ *   - head_dim: 32, 64 or 128 for bf16; 16, 32, 64 or 128 for fp32.
+ *     Pointers must be 16-byte aligned.  chunk_frames >= 1, overlap_frames >= 0
+ *     (overlap_frames >= chunk_frames is allowed); the last chunk may be partial.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL = the
+ *     null stream).  Arguments are validated on the host before any GPU work is
+ *     queued; on failure nothing is queued, the status is returned and
+ *     rehyat_last_error() describes it.  Errors raised by the HIP runtime while
+ *     queueing map to REHYAT_EHIP.  No call aborts or throws across the ABI.
+ */
+#ifndef REHYAT_H
+#define REHYAT_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rehyat_feature_map {
+    REHYAT_PHI_NONE = 0,  /* no linear branch: softmax over the local window only */
+    REHYAT_PHI_ELU1 = 1,  /* phi(x) = elu(x) + 1 (alpha 1), D' = head_dim (§3.1) */
+    REHYAT_PHI_POLY2 = 2  /* phi(x) = [elu(x) + 1, x*x], D' = 2 head_dim: a parameter-free
+                             degree-2 instance of the polynomial map of §3.2 */
+} rehyat_feature_map;
+
+typedef enum rehyat_status {
+    REHYAT_OK = 0,
+    REHYAT_EINVAL = 1,        /* invalid argument (null pointer, bad size, misalignment) */
+    REHYAT_EUNSUPPORTED = 2,  /* valid but not built (head_dim, dtype, feature map) */
+    REHYAT_ENOMEM = 3,        /* device workspace could not be allocated */
+    REHYAT_EHIP = 4           /* the HIP runtime reported an error */
+} rehyat_status;
+
+typedef enum rehyat_dtype { REHYAT_F32 = 0, REHYAT_BF16 = 1 } rehyat_dtype;
+
+/*
+ * Whole-clip forward, parallel chunked form (§3.2-§3.3).
+ *   q, k, v : in,  [B][H][frames*tokens_per_frame][head_dim] bf16
+ *   out     : out, same shape and dtype; must not alias q, k or v
+ * A transient fp32 workspace (about ceil(F/T_c) * B * H * (D' head_dim + D') * 12 bytes)
+ * comes from a per-device arena the library grows on demand and keeps for
+ * the life of the process (REHYAT_ENOMEM if it cannot grow).  With
+ * chunk_frames >= frames and REHYAT_PHI_NONE this is plain bidirectional
+ * softmax attention (the dense comparison point).
+ */
+rehyat_status rehyat_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                              int B, int H, int frames, int tokens_per_frame, int head_dim,
+                              int chunk_frames, int overlap_frames, int feature_map,
+                              void* stream);
+
+/* Same contract with fp32 q, k, v, out. */
+rehyat_status rehyat_attn_fwd_f32(const void* q, const void* k, const void* v, void* out,
+                                  int B, int H, int frames, int tokens_per_frame, int head_dim,
+                                  int chunk_frames, int overlap_frames, int feature_map,
+                                  void* stream);
+
+/*
+ * Forward that writes per-query partials instead of `out` (a verification aid:
+ * it lets each branch be checked on its own).  Same kernels as rehyat_attn_fwd.
+ * dtype selects bf16 or fp32 inputs.  Outputs are caller-owned fp32 device
+ * arrays; each may be NULL:
+ *   m   [B][H][N]     max of q.k over the softmax set
+ *   nt  [B][H][N]     sum over the softmax set of exp(q.k - m)
+ *   o_s [B][H][N][d]  softmax-branch output a^S / n^S
+ *   o_l [B][H][N][d]  linear-branch output a^L / n^L (0 where n^L = 0)
+ *   n_l [B][H][N]     n^L
+ */
+rehyat_status rehyat_attn_fwd_partials(const void* q, const void* k, const void* v, int dtype,
+                                       float* m, float* nt, float* o_s, float* o_l, float* n_l,
+                                       int B, int H, int frames, int tokens_per_frame,
+                                       int head_dim, int chunk_frames, int overlap_frames,
+                                       int feature_map, void* stream);
+
+/*
+ * Streaming (chunk-wise RNN) form, §3.3: one call per chunk of frames, with
+ * memory that does not depend on how many frames have been processed.
+ *
+ * The state lives in one caller-owned device buffer of
+ * rehyat_step_state_bytes() bytes plus this host struct.  It holds the fp32
+ * linear state (S, z) of every key that has left the softmax window, the keys
+ * and values of the last min(overlap_frames, frames so far) frames, and a
+ * small fp32 workspace.  Its contents need no initialisation: a freshly
+ * initialised state (frames_done == 0) never reads them.  Saving the buffer
+ * and the struct and restoring both resumes the stream exactly.
+ */
+typedef struct rehyat_step_state {
+    void* buf;              /* device buffer, caller-owned */
+    size_t bytes;           /* its size */
+    int B, H, tokens_per_frame, head_dim, chunk_frames, overlap_frames, feature_map, dtype;
+    int prev_frames;        /* frames of K/V held for the next window (library-maintained) */
+    int prev_slot;          /* which of the two K/V slots holds them (library-maintained) */
+    int state_nonempty;     /* (S, z) has absorbed at least one key (library-maintained) */
+    long long frames_done;  /* frames processed so far (library-maintained) */
+} rehyat_step_state;
+
+/* Bytes of device buffer the state needs; 0 if the arguments are invalid. */
+size_t rehyat_step_state_bytes(int B, int H, int tokens_per_frame, int head_dim,
+                               int chunk_frames, int overlap_frames, int feature_map, int dtype);
+
+/* Validate the geometry and bind `buf` (at least rehyat_step_state_bytes()).
+ * Host only: queues no GPU work. */
+rehyat_status rehyat_step_state_init(rehyat_step_state* st, void* buf, size_t bytes, int B, int H,
+                                     int tokens_per_frame, int head_dim, int chunk_frames,
+                                     int overlap_frames, int feature_map, int dtype);
+
+/*
+ * Attend one chunk: q, k, v, out are [B][H][frames*tokens_per_frame][head_dim]
+ * in the state's dtype, 1 <= frames <= chunk_frames.  Every call but the last
+ * of a stream must pass frames == chunk_frames; then the concatenated outputs
+ * equal rehyat_attn_fwd on the concatenated inputs.  Updates `st`.
+ * Concurrent calls on one state are not allowed.
+ */
+rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void* k, const void* v,
+                               void* out, int frames, void* stream);
+
+/*
+ * Profiling aid.  While set on the calling thread, every whole-clip forward
+ * call records four hipEvent_t handles on its stream: events[0] before the
+ * block-state kernel, events[1] before the scan kernel, events[2] before the
+ * local-softmax kernel and events[3] after it (events[0..2] coincide when the
+ * call has no linear branch).  Pass (NULL, 0) to stop.  The events are owned by
+ * the caller and must stay valid until the calls that record them complete.
+ * n_events must be 0 or 4.
+ */
+rehyat_status rehyat_set_profile_events(void* const* events, int n_events);
+
+/* Static description of a status code. */
+const char* rehyat_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* rehyat_last_error(void);
+
+/* Library version string. */
+const char* rehyat_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REHYAT_H */

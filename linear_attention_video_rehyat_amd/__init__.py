@@ -1,0 +1,250 @@
+"""Python binding of librehyat (ReHyAt recurrent hybrid attention forward, MI355X).
+
+Argument marshalling only: torch supplies device memory and the stream; every
+step of the computation runs in the HIP kernels of ``librehyat.so``.  The
+library must be built first (``python -m linear_attention_video_rehyat_amd.build``);
+calls raise :class:`RehyatError` if it is missing -- there is no fallback.
+
+Method: "ReHyAt: Recurrent Hybrid Attention for Video Diffusion Transformers"
+(arXiv 2601.04342): local softmax over each temporal chunk plus the T_o frames
+before it, feature-mapped linear attention over every earlier key carried as a
+chunk-wise RNN state, joint normalisation of the two branches (§3.1-§3.3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["RehyatError", "attn_fwd", "attn_fwd_partials", "StepState", "feature_map_id",
+           "library_path", "load_library", "exported_symbols"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "librehyat.so")
+_lib = None
+
+FEATURE_MAPS = {"none": 0, "elu1": 1, "poly2": 2}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+# every entry point declared in include/rehyat.h
+exported_symbols = (
+    "rehyat_attn_fwd", "rehyat_attn_fwd_f32", "rehyat_attn_fwd_partials",
+    "rehyat_step_state_bytes", "rehyat_step_state_init", "rehyat_attn_step",
+    "rehyat_set_profile_events", "rehyat_status_string", "rehyat_last_error", "rehyat_version",
+)
+
+
+class RehyatError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class _StepStateC(ctypes.Structure):
+    _fields_ = [
+        ("buf", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("tokens_per_frame", ctypes.c_int),
+        ("head_dim", ctypes.c_int), ("chunk_frames", ctypes.c_int), ("overlap_frames", ctypes.c_int),
+        ("feature_map", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("prev_frames", ctypes.c_int), ("prev_slot", ctypes.c_int), ("state_nonempty", ctypes.c_int),
+        ("frames_done", ctypes.c_longlong),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load librehyat.so (raises RehyatError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RehyatError(-1, f"librehyat.so not found at {_LIB_PATH}; build it with "
+                              "`python -m linear_attention_video_rehyat_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f_p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float)
+    sig_fwd = [vp, vp, vp, vp] + [i] * 8 + [vp]
+    for name in ("rehyat_attn_fwd", "rehyat_attn_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes, fn.restype = sig_fwd, i
+    lib.rehyat_attn_fwd_partials.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp] + [i] * 8 + [vp]
+    lib.rehyat_attn_fwd_partials.restype = i
+    lib.rehyat_step_state_bytes.argtypes = [i] * 8
+    lib.rehyat_step_state_bytes.restype = ctypes.c_size_t
+    lib.rehyat_step_state_init.argtypes = [ctypes.POINTER(_StepStateC), vp, ctypes.c_size_t] + [i] * 8
+    lib.rehyat_step_state_init.restype = i
+    lib.rehyat_attn_step.argtypes = [ctypes.POINTER(_StepStateC), vp, vp, vp, vp, i, vp]
+    lib.rehyat_attn_step.restype = i
+    lib.rehyat_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
+    lib.rehyat_set_profile_events.restype = i
+    lib.rehyat_status_string.argtypes = [i]
+    lib.rehyat_status_string.restype = ctypes.c_char_p
+    lib.rehyat_last_error.argtypes = []
+    lib.rehyat_last_error.restype = ctypes.c_char_p
+    lib.rehyat_version.argtypes = []
+    lib.rehyat_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        msg = f"{lib.rehyat_status_string(status).decode()}: {lib.rehyat_last_error().decode()}"
+        raise RehyatError(status, msg)
+
+
+def feature_map_id(fm) -> int:
+    if isinstance(fm, str):
+        return FEATURE_MAPS[fm.lower()]
+    return int(fm)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_id(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise RehyatError(2, f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise RehyatError(1, f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise RehyatError(1, f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise RehyatError(1, f"{name} must be [B, H, N, head_dim]")
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise RehyatError(1, "q, k, v must have the same shape and dtype")
+
+
+def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, feature_map="elu1",
+             out=None, stream=None):
+    """Whole-clip hybrid attention forward.  q, k, v: [B, H, frames*tokens_per_frame, d]
+    (bf16 or fp32, contiguous, on the GPU).  Returns ``out`` (allocated if None)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if N != frames * tokens_per_frame:
+        raise RehyatError(1, f"N={N} != frames*tokens_per_frame={frames * tokens_per_frame}")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise RehyatError(1, "out must match q")
+    fn = lib.rehyat_attn_fwd if _dtype_id(q) == DTYPE_BF16 else lib.rehyat_attn_fwd_f32
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, frames,
+              tokens_per_frame, d, chunk_frames, overlap_frames, feature_map_id(feature_map),
+              _stream_handle(stream)))
+    return out
+
+
+def attn_fwd_partials(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames,
+                      feature_map="elu1", stream=None):
+    """Per-query partials of both branches (verification aid): dict with m, nt,
+    o_s, o_l, n_l as fp32 tensors (see include/rehyat.h)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    f32 = dict(dtype=torch.float32, device=q.device)
+    parts = {"m": torch.empty(B, H, N, **f32), "nt": torch.empty(B, H, N, **f32),
+             "o_s": torch.empty(B, H, N, d, **f32), "o_l": torch.empty(B, H, N, d, **f32),
+             "n_l": torch.empty(B, H, N, **f32)}
+    _check(lib.rehyat_attn_fwd_partials(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_id(q),
+        parts["m"].data_ptr(), parts["nt"].data_ptr(), parts["o_s"].data_ptr(),
+        parts["o_l"].data_ptr(), parts["n_l"].data_ptr(), B, H, frames, tokens_per_frame, d,
+        chunk_frames, overlap_frames, feature_map_id(feature_map), _stream_handle(stream)))
+    return parts
+
+
+def set_profile_events(events):
+    """Record 4 caller-owned hipEvent_t handles around the kernels of every
+    forward call on this thread (see include/rehyat.h); None to stop."""
+    lib = load_library()
+    if events is None:
+        _check(lib.rehyat_set_profile_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e)) for e in events])
+    _check(lib.rehyat_set_profile_events(arr, 4))
+
+
+class StepState:
+    """Streaming (chunk-wise RNN) state: a device buffer owned by this object
+    plus the library's host header.  ``step`` attends one chunk of frames."""
+
+    def __init__(self, B, H, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
+                 feature_map="elu1", dtype=None, device="cuda"):
+        torch = _torch()
+        lib = load_library()
+        dtype = torch.bfloat16 if dtype is None else dtype
+        self.dtype = dtype
+        did = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+        fm = feature_map_id(feature_map)
+        nbytes = lib.rehyat_step_state_bytes(B, H, tokens_per_frame, head_dim, chunk_frames,
+                                             overlap_frames, fm, did)
+        if nbytes == 0:  # invalid geometry: let init report why
+            probe = _StepStateC()
+            _check(lib.rehyat_step_state_init(ctypes.byref(probe), None, 0, B, H, tokens_per_frame,
+                                              head_dim, chunk_frames, overlap_frames, fm, did))
+        self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+        self._c = _StepStateC()
+        _check(lib.rehyat_step_state_init(ctypes.byref(self._c), self.buf.data_ptr(), int(nbytes),
+                                          B, H, tokens_per_frame, head_dim, chunk_frames,
+                                          overlap_frames, fm, did))
+        self.shape = (B, H, tokens_per_frame, head_dim)
+
+    @property
+    def nbytes(self) -> int:
+        return int(self._c.bytes)
+
+    @property
+    def frames_done(self) -> int:
+        return int(self._c.frames_done)
+
+    def header(self) -> dict:
+        return {name: getattr(self._c, name) for name, _ in _StepStateC._fields_ if name != "buf"}
+
+    def step(self, q, k, v, out=None, stream=None):
+        torch = _torch()
+        lib = load_library()
+        _check_qkv(q, k, v)
+        if q.dtype != self.dtype:
+            raise RehyatError(1, f"chunk dtype {q.dtype} != state dtype {self.dtype}")
+        B, H, n, d = q.shape
+        HW = self._c.tokens_per_frame
+        if n % HW != 0:
+            raise RehyatError(1, f"chunk rows {n} not a multiple of tokens_per_frame {HW}")
+        if out is None:
+            out = torch.empty_like(q)
+        _check(lib.rehyat_attn_step(ctypes.byref(self._c), q.data_ptr(), k.data_ptr(),
+                                    v.data_ptr(), out.data_ptr(), n // HW, _stream_handle(stream)))
+        return out
+
+    def save(self):
+        """(host copy of the device buffer, header) -- a checkpoint of the stream."""
+        return self.buf.cpu().clone(), self.header()
+
+    def restore(self, saved):
+        buf, header = saved
+        self.buf.copy_(buf)
+        for name, value in header.items():
+            if name != "bytes":
+                setattr(self._c, name, value)

@@ -1,0 +1,459 @@
+// api.cpp -- the C ABI of librehyat: argument validation, chunk geometry,
+// workspace management and launch sequencing.  See include/rehyat.h.
+//
+// Geometry (ReHyAt, arXiv 2601.04342, §3.3 equation; N' = T_c HW): chunk t owns
+// frames [t T_c, min((t+1) T_c, F)); its softmax window starts T_o frames
+// earlier (clipped at 0); its linear set is every key before the window.  The
+// keys leaving the window between chunk u and u+1 form the delta block
+// E_u = frames [max(u T_c - T_o, 0), max((u+1) T_c - T_o, 0)), so the state of
+// chunk t is the sum over u < t of the block sums (the chunk-wise RNN form).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/rehyat.h"
+#include "kernels.h"
+
+using namespace rehyat;
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_prof[4] = {nullptr, nullptr, nullptr, nullptr};
+
+hipError_t prof_mark(int i, hipStream_t s) {
+    return g_prof[i] ? hipEventRecord(g_prof[i], s) : hipSuccess;
+}
+
+rehyat_status fail(rehyat_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+rehyat_status hip_fail(hipError_t e, const char* what) {
+    return fail(REHYAT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kStateSubRows = 1024;  // key rows per block-state workgroup
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bf16_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool f32_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Geometry {
+    int B, H, F, HW, d, Tc, To, phi, dtype;
+    long long N;      // tokens per (b, h)
+    int BH, C, Dp, E; // chunks, feature dim, state elements (d*Dp + Dp)
+    int elem;         // bytes per element of q/k/v/out
+};
+
+rehyat_status check_common(Geometry& g, int B, int H, int frames, int tpf, int d, int Tc, int To,
+                           int phi, int dtype) {
+    if (B < 1 || H < 1) return fail(REHYAT_EINVAL, "B and H must be >= 1 (got B=%d H=%d)", B, H);
+    if (frames < 1 || tpf < 1)
+        return fail(REHYAT_EINVAL, "frames and tokens_per_frame must be >= 1 (got %d, %d)", frames, tpf);
+    if (Tc < 1) return fail(REHYAT_EINVAL, "chunk_frames must be >= 1 (got %d)", Tc);
+    if (To < 0) return fail(REHYAT_EINVAL, "overlap_frames must be >= 0 (got %d)", To);
+    if (phi < REHYAT_PHI_NONE || phi > REHYAT_PHI_POLY2)
+        return fail(REHYAT_EINVAL, "unknown feature_map %d", phi);
+    if (dtype != REHYAT_F32 && dtype != REHYAT_BF16) return fail(REHYAT_EINVAL, "unknown dtype %d", dtype);
+    if (dtype == REHYAT_BF16 && !bf16_dim_ok(d))
+        return fail(REHYAT_EUNSUPPORTED, "head_dim %d not supported for bf16 (32, 64, 128)", d);
+    if (dtype == REHYAT_F32 && !f32_dim_ok(d))
+        return fail(REHYAT_EUNSUPPORTED, "head_dim %d not supported for fp32 (16, 32, 64, 128)", d);
+    const long long N = (long long)frames * tpf;
+    if (N > (1LL << 30)) return fail(REHYAT_EINVAL, "frames*tokens_per_frame = %lld is too large", N);
+    const long long BH = (long long)B * H;
+    if (BH > (1LL << 24)) return fail(REHYAT_EINVAL, "B*H = %lld is too large", BH);
+    g.B = B; g.H = H; g.F = frames; g.HW = tpf; g.d = d; g.Tc = Tc; g.To = To; g.phi = phi; g.dtype = dtype;
+    g.N = N;
+    g.BH = (int)BH;
+    g.C = (frames + Tc - 1) / Tc;
+    g.Dp = feature_dim(phi, d);
+    g.E = d * g.Dp + g.Dp;
+    g.elem = dtype == REHYAT_BF16 ? 2 : 4;
+    return REHYAT_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// ---------------------------------------------------------------- workspace arena
+struct Arena {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_arena_mu;
+std::vector<Arena> g_arenas;
+
+rehyat_status arena_get(size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_arena_mu);
+    if ((int)g_arenas.size() <= dev) g_arenas.resize(dev + 1);
+    Arena& a = g_arenas[dev];
+    if (a.bytes < bytes) {
+        if (a.ptr) {
+            // earlier calls may still be using the old buffer
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            (void)hipFree(a.ptr);
+            a.ptr = nullptr;
+            a.bytes = 0;
+        }
+        size_t want = bytes + bytes / 4 + (1u << 20);
+        e = hipMalloc(&a.ptr, want);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            a.ptr = nullptr;
+            return fail(REHYAT_ENOMEM, "cannot allocate %zu bytes of workspace: %s", want, hipGetErrorString(e));
+        }
+        a.bytes = want;
+    }
+    *out = a.ptr;
+    return REHYAT_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace of the whole-clip forward: partial block sums and prepared states.
+struct FwdWorkspace {
+    size_t partial_off, shi_off, slo_off, z_off, total;
+    int U, n_sub;
+};
+
+FwdWorkspace fwd_workspace(const Geometry& g) {
+    FwdWorkspace w{};
+    w.U = g.C - 1;
+    w.n_sub = (g.Tc * g.HW + kStateSubRows - 1) / kStateSubRows;
+    const size_t partial = (size_t)g.BH * w.U * w.n_sub * g.E * 4;
+    const size_t sprep = (size_t)g.BH * g.C * g.d * g.Dp * (g.dtype == REHYAT_BF16 ? 2 : 4);
+    const size_t zprep = (size_t)g.BH * g.C * g.Dp * 4;
+    w.partial_off = 0;
+    w.shi_off = align256(partial);
+    w.slo_off = w.shi_off + align256(sprep);
+    w.z_off = w.slo_off + (g.dtype == REHYAT_BF16 ? align256(sprep) : 0);
+    w.total = w.z_off + align256(zprep);
+    return w;
+}
+
+// A chunk t has a linear set iff t T_c - T_o > 0; the last chunk is t = C-1.
+bool any_linear(const Geometry& g) {
+    return g.phi != REHYAT_PHI_NONE && (long long)(g.C - 1) * g.Tc - g.To > 0;
+}
+
+rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g,
+                      float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s) {
+    const bool lin = any_linear(g);
+    char* ws = nullptr;
+    FwdWorkspace w{};
+    hipError_t pe = prof_mark(0, s);
+    if (pe != hipSuccess) return hip_fail(pe, "hipEventRecord");
+    if (lin) {
+        w = fwd_workspace(g);
+        void* p = nullptr;
+        rehyat_status st = arena_get(w.total, &p);
+        if (st != REHYAT_OK) return st;
+        ws = (char*)p;
+
+        StateParams sp{};
+        sp.k = k; sp.v = v; sp.kp = nullptr; sp.vp = nullptr;
+        sp.bh_stride = g.N * g.d; sp.prev_bh_stride = 0; sp.prev_rows = 0;
+        sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
+        sp.n_blocks = w.U; sp.sub_rows = kStateSubRows; sp.n_sub = w.n_sub; sp.stream_rows = 0;
+        sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
+        sp.partial = (float*)(ws + w.partial_off);
+        hipError_t e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
+        if (e != hipSuccess) return hip_fail(e, "block-state launch");
+        if ((e = prof_mark(1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+        ScanParams cp{};
+        cp.partial = sp.partial; cp.init = nullptr; cp.state_out = nullptr;
+        cp.s_hi = ws + w.shi_off; cp.s_lo = ws + w.slo_off; cp.z = (float*)(ws + w.z_off);
+        cp.s_chunk_stride = (long long)g.d * g.Dp; cp.s_bh_stride = (long long)g.C * g.d * g.Dp;
+        cp.z_chunk_stride = g.Dp; cp.z_bh_stride = (long long)g.C * g.Dp;
+        cp.U = w.U; cp.n_sub = w.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
+        cp.t_first = 1; cp.t_offset = 0; cp.f32_prep = g.dtype == REHYAT_F32;
+        e = launch_scan(cp, s);
+        if (e != hipSuccess) return hip_fail(e, "scan launch");
+    } else {
+        if ((pe = prof_mark(1, s)) != hipSuccess) return hip_fail(pe, "hipEventRecord");
+    }
+    if ((pe = prof_mark(2, s)) != hipSuccess) return hip_fail(pe, "hipEventRecord");
+    LocalParams lp{};
+    lp.q = q; lp.out = out; lp.k = k; lp.v = v; lp.kp = nullptr; lp.vp = nullptr;
+    lp.bh_stride = g.N * g.d; lp.prev_bh_stride = 0; lp.prev_rows = 0;
+    lp.HW = g.HW; lp.F = g.F; lp.Tc = g.Tc; lp.To = g.To;
+    lp.n_chunks = g.C; lp.BH = g.BH; lp.d = g.d;
+    const int bm = g.dtype == REHYAT_BF16 ? local_bf16_tile_rows(g.d) : local_f32_tile_rows(g.d);
+    const long long rows_per_chunk = (long long)std::min<long long>(g.Tc, g.F) * g.HW;
+    lp.tiles_per_chunk = (int)((rows_per_chunk + bm - 1) / bm);
+    const long long blocks = (long long)g.BH * g.C * lp.tiles_per_chunk;
+    if (blocks > 0x7fffffffLL) return fail(REHYAT_EINVAL, "problem too large: %lld workgroups", blocks);
+    lp.phi = g.phi; lp.lin_always = 0;
+    if (lin) {
+        lp.s_hi = ws + w.shi_off; lp.s_lo = ws + w.slo_off; lp.z = (const float*)(ws + w.z_off);
+        lp.s_chunk_stride = (long long)g.d * g.Dp; lp.s_bh_stride = (long long)g.C * g.d * g.Dp;
+        lp.z_chunk_stride = g.Dp; lp.z_bh_stride = (long long)g.C * g.Dp;
+    } else {
+        lp.phi = REHYAT_PHI_NONE;  // no chunk has a linear set
+    }
+    lp.pm = pm; lp.pnt = pnt; lp.poS = poS; lp.poL = poL; lp.pnL = pnL;
+    hipError_t e = g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s);
+    if (e != hipSuccess) return hip_fail(e, "local-attention launch");
+    if ((e = prof_mark(3, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return REHYAT_OK;
+}
+
+rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, int B, int H,
+                        int frames, int tpf, int d, int Tc, int To, int phi, int dtype, void* stream) {
+    Geometry g{};
+    rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
+    if (st != REHYAT_OK) return st;
+    if (!q || !k || !v || !out) return fail(REHYAT_EINVAL, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(REHYAT_EINVAL, "tensor pointers must be 16-byte aligned");
+    const size_t bytes = (size_t)g.BH * g.N * g.d * g.elem;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+        return fail(REHYAT_EINVAL, "out must not overlap q, k or v");
+    g_last_error.clear();
+    return run_fwd(q, k, v, out, g, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- streaming state
+struct StepLayout {
+    size_t S_off, shi_off, slo_off, z_off, kp_off[2], vp_off[2], partial_off, total;
+    int n_sub;
+    size_t prev_bytes;  // one K (or V) slot
+};
+
+StepLayout step_layout(const Geometry& g) {
+    StepLayout L{};
+    const size_t E = (size_t)g.E;
+    L.n_sub = (g.Tc * g.HW + kStateSubRows - 1) / kStateSubRows;
+    size_t off = 0;
+    L.S_off = off; off += align256((size_t)g.BH * E * 4);
+    const size_t sprep = (size_t)g.BH * g.d * g.Dp * (g.dtype == REHYAT_BF16 ? 2 : 4);
+    L.shi_off = off; off += align256(sprep);
+    L.slo_off = off; off += g.dtype == REHYAT_BF16 ? align256(sprep) : 0;
+    L.z_off = off; off += align256((size_t)g.BH * g.Dp * 4);
+    L.prev_bytes = (size_t)g.BH * g.To * g.HW * g.d * g.elem;
+    for (int i = 0; i < 2; ++i) {
+        L.kp_off[i] = off; off += align256(L.prev_bytes);
+        L.vp_off[i] = off; off += align256(L.prev_bytes);
+    }
+    L.partial_off = off; off += align256((size_t)g.BH * L.n_sub * E * 4);
+    L.total = off > 256 ? off : 256;  // never 0: 0 means "invalid arguments"
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+rehyat_status rehyat_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H,
+                              int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+                              int overlap_frames, int feature_map, void* stream) {
+    return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
+                     overlap_frames, feature_map, REHYAT_BF16, stream);
+}
+
+rehyat_status rehyat_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, int B,
+                                  int H, int frames, int tokens_per_frame, int head_dim,
+                                  int chunk_frames, int overlap_frames, int feature_map,
+                                  void* stream) {
+    return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
+                     overlap_frames, feature_map, REHYAT_F32, stream);
+}
+
+rehyat_status rehyat_attn_fwd_partials(const void* q, const void* k, const void* v, int dtype,
+                                       float* m, float* nt, float* o_s, float* o_l, float* n_l,
+                                       int B, int H, int frames, int tokens_per_frame,
+                                       int head_dim, int chunk_frames, int overlap_frames,
+                                       int feature_map, void* stream) {
+    Geometry g{};
+    rehyat_status st = check_common(g, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
+                                    overlap_frames, feature_map, dtype);
+    if (st != REHYAT_OK) return st;
+    if (!q || !k || !v) return fail(REHYAT_EINVAL, "null tensor pointer");
+    if (!m && !nt && !o_s && !o_l && !n_l) return fail(REHYAT_EINVAL, "no partial output requested");
+    const void* ptrs[8] = {q, k, v, m, nt, o_s, o_l, n_l};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(REHYAT_EINVAL, "pointers must be 16-byte aligned");
+    g_last_error.clear();
+    return run_fwd(q, k, v, nullptr, g, m, nt, o_s, o_l, n_l, (hipStream_t)stream);
+}
+
+size_t rehyat_step_state_bytes(int B, int H, int tokens_per_frame, int head_dim, int chunk_frames,
+                               int overlap_frames, int feature_map, int dtype) {
+    Geometry g{};
+    if (check_common(g, B, H, chunk_frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
+                     feature_map, dtype) != REHYAT_OK)
+        return 0;
+    return step_layout(g).total;
+}
+
+rehyat_status rehyat_step_state_init(rehyat_step_state* st, void* buf, size_t bytes, int B, int H,
+                                     int tokens_per_frame, int head_dim, int chunk_frames,
+                                     int overlap_frames, int feature_map, int dtype) {
+    if (!st) return fail(REHYAT_EINVAL, "null state");
+    Geometry g{};
+    rehyat_status s = check_common(g, B, H, chunk_frames, tokens_per_frame, head_dim, chunk_frames,
+                                   overlap_frames, feature_map, dtype);
+    if (s != REHYAT_OK) return s;
+    const size_t need = step_layout(g).total;
+    if (!buf) return fail(REHYAT_EINVAL, "null state buffer");
+    if (!aligned16(buf)) return fail(REHYAT_EINVAL, "state buffer must be 16-byte aligned");
+    if (bytes < need) return fail(REHYAT_EINVAL, "state buffer too small: %zu < %zu bytes", bytes, need);
+    std::memset(st, 0, sizeof(*st));
+    st->buf = buf;
+    st->bytes = bytes;
+    st->B = B; st->H = H; st->tokens_per_frame = tokens_per_frame; st->head_dim = head_dim;
+    st->chunk_frames = chunk_frames; st->overlap_frames = overlap_frames;
+    st->feature_map = feature_map; st->dtype = dtype;
+    g_last_error.clear();
+    return REHYAT_OK;
+}
+
+rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void* k, const void* v,
+                               void* out, int frames, void* stream) {
+    if (!st || !st->buf) return fail(REHYAT_EINVAL, "state not initialised");
+    Geometry g{};
+    rehyat_status s0 = check_common(g, st->B, st->H, st->chunk_frames, st->tokens_per_frame,
+                                    st->head_dim, st->chunk_frames, st->overlap_frames,
+                                    st->feature_map, st->dtype);
+    if (s0 != REHYAT_OK) return s0;
+    const StepLayout L = step_layout(g);
+    if (st->bytes < L.total) return fail(REHYAT_EINVAL, "state buffer too small");
+    if (frames < 1 || frames > st->chunk_frames)
+        return fail(REHYAT_EINVAL, "frames must be in [1, chunk_frames=%d] (got %d)", st->chunk_frames, frames);
+    if (st->frames_done % st->chunk_frames != 0)
+        return fail(REHYAT_EINVAL, "the stream already ended with a partial chunk");
+    if (st->prev_frames < 0 || st->prev_frames > st->overlap_frames || (st->prev_slot & ~1))
+        return fail(REHYAT_EINVAL, "corrupt state header");
+    if (!q || !k || !v || !out) return fail(REHYAT_EINVAL, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(REHYAT_EINVAL, "tensor pointers must be 16-byte aligned");
+    const long long n = (long long)frames * g.HW;
+    const size_t bytes = (size_t)g.BH * n * g.d * g.elem;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes) ||
+        overlaps(out, bytes, st->buf, st->bytes))
+        return fail(REHYAT_EINVAL, "out must not overlap q, k, v or the state buffer");
+    g_last_error.clear();
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)st->buf;
+    const int P = st->prev_frames * g.HW;
+    const int cur = st->prev_slot;
+
+    // 1. local softmax over [prev | chunk] + linear branch from the carried state
+    LocalParams lp{};
+    lp.q = q; lp.out = out; lp.k = k; lp.v = v;
+    lp.kp = P > 0 ? base + L.kp_off[cur] : nullptr;
+    lp.vp = P > 0 ? base + L.vp_off[cur] : nullptr;
+    lp.bh_stride = n * g.d;
+    lp.prev_bh_stride = (long long)g.To * g.HW * g.d;
+    lp.prev_rows = P;
+    lp.HW = g.HW; lp.F = frames; lp.Tc = frames; lp.To = 0;
+    lp.n_chunks = 1; lp.BH = g.BH; lp.d = g.d;
+    const int bm = g.dtype == REHYAT_BF16 ? local_bf16_tile_rows(g.d) : local_f32_tile_rows(g.d);
+    lp.tiles_per_chunk = (int)((n + bm - 1) / bm);
+    lp.phi = g.phi;
+    lp.lin_always = (g.phi != REHYAT_PHI_NONE && st->state_nonempty) ? 1 : 0;
+    if (!lp.lin_always) lp.phi = REHYAT_PHI_NONE;
+    lp.s_hi = base + L.shi_off; lp.s_lo = base + L.slo_off; lp.z = (const float*)(base + L.z_off);
+    lp.s_chunk_stride = 0; lp.s_bh_stride = (long long)g.d * g.Dp;
+    lp.z_chunk_stride = 0; lp.z_bh_stride = g.Dp;
+    hipError_t e = g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s);
+    if (e != hipSuccess) return hip_fail(e, "local-attention launch");
+
+    // 2. fold the rows leaving the window into (S, z)
+    const long long done = st->frames_done + frames;
+    const int keep_frames = (int)std::min<long long>(g.To, done);
+    const int keep_rows = keep_frames * g.HW;
+    const int evict_rows = P + (int)n - keep_rows;
+    bool nonempty = st->state_nonempty != 0;
+    if (g.phi != REHYAT_PHI_NONE && evict_rows > 0) {
+        StateParams sp{};
+        sp.k = k; sp.v = v; sp.kp = lp.kp; sp.vp = lp.vp;
+        sp.bh_stride = n * g.d; sp.prev_bh_stride = lp.prev_bh_stride; sp.prev_rows = P;
+        sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
+        sp.n_blocks = 1; sp.sub_rows = kStateSubRows;
+        sp.n_sub = (evict_rows + kStateSubRows - 1) / kStateSubRows;
+        sp.stream_rows = evict_rows;
+        sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
+        sp.partial = (float*)(base + L.partial_off);
+        e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
+        if (e != hipSuccess) return hip_fail(e, "block-state launch");
+        ScanParams cp{};
+        cp.partial = sp.partial;
+        cp.init = nonempty ? (const float*)(base + L.S_off) : nullptr;
+        cp.state_out = (float*)(base + L.S_off);
+        cp.s_hi = base + L.shi_off; cp.s_lo = base + L.slo_off; cp.z = (float*)(base + L.z_off);
+        cp.s_chunk_stride = 0; cp.s_bh_stride = (long long)g.d * g.Dp;
+        cp.z_chunk_stride = 0; cp.z_bh_stride = g.Dp;
+        cp.U = 1; cp.n_sub = sp.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
+        cp.t_first = 1; cp.t_offset = 1; cp.f32_prep = g.dtype == REHYAT_F32;
+        e = launch_scan(cp, s);
+        if (e != hipSuccess) return hip_fail(e, "scan launch");
+        nonempty = true;
+    }
+    // 3. keep the last min(T_o, frames so far) frames for the next window
+    if (keep_rows > 0) {
+        PrevCopyParams pc{};
+        pc.kp = lp.kp; pc.vp = lp.vp; pc.prev_bh_stride = lp.prev_bh_stride; pc.prev_rows = P;
+        pc.k = k; pc.v = v; pc.bh_stride = n * g.d; pc.chunk_rows = (int)n;
+        pc.kd = base + L.kp_off[cur ^ 1]; pc.vd = base + L.vp_off[cur ^ 1];
+        pc.keep_rows = keep_rows; pc.BH = g.BH; pc.d = g.d; pc.elem_bytes = g.elem;
+        e = launch_prev_copy(pc, s);
+        if (e != hipSuccess) return hip_fail(e, "overlap copy launch");
+    }
+    st->prev_slot = keep_rows > 0 ? cur ^ 1 : cur;
+    st->prev_frames = keep_frames;
+    st->state_nonempty = nonempty ? 1 : 0;
+    st->frames_done = done;
+    return REHYAT_OK;
+}
+
+rehyat_status rehyat_set_profile_events(void* const* events, int n_events) {
+    if (n_events == 0) {
+        for (auto& e : g_prof) e = nullptr;
+        return REHYAT_OK;
+    }
+    if (n_events != 4 || !events) return fail(REHYAT_EINVAL, "n_events must be 0 or 4");
+    for (int i = 0; i < 4; ++i)
+        if (!events[i]) return fail(REHYAT_EINVAL, "null event");
+    for (int i = 0; i < 4; ++i) g_prof[i] = (hipEvent_t)events[i];
+    return REHYAT_OK;
+}
+
+const char* rehyat_status_string(int status) {
+    switch (status) {
+    case REHYAT_OK: return "ok";
+    case REHYAT_EINVAL: return "invalid argument";
+    case REHYAT_EUNSUPPORTED: return "unsupported configuration";
+    case REHYAT_ENOMEM: return "out of device memory";
+    case REHYAT_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* rehyat_last_error(void) { return g_last_error.c_str(); }
+
+const char* rehyat_version(void) { return "librehyat 0.1.0 (gfx950)"; }
+
+}  // extern "C"

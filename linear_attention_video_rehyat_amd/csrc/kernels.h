@@ -1,0 +1,93 @@
+// kernels.h -- host-side launch interface between the C ABI (api.cpp) and the
+// HIP kernels.  Plain structs of pointers and sizes; no torch types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rehyat {
+
+enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiPoly2 = 2 };
+
+inline int feature_dim(int phi, int d) { return phi == kPhiElu1 ? d : (phi == kPhiPoly2 ? 2 * d : 0); }
+
+// Local-softmax + fused hybrid combine (one launch covers every (b, h, chunk,
+// query tile)).  Key rows of a window are addressed through a virtual index j:
+// j < prev_rows reads the "prev" segment (the streaming overlap frames), the
+// rest read the clip from row w0 of the chunk's window.
+struct LocalParams {
+    const void* q;            // [BH][n_rows][d] queries (clip or chunk)
+    void* out;                // same layout as q
+    const void* k;            // [BH][n_rows][d]
+    const void* v;
+    const void* kp;           // [BH][prev_stride_rows][d] overlap segment (streaming), or null
+    const void* vp;
+    long long bh_stride;      // n_rows * d
+    long long prev_bh_stride; // rows per (b,h) in kp/vp times d
+    int prev_rows;            // rows of the overlap segment in front of the window
+    int HW, F, Tc, To;        // frames / chunk geometry of this launch
+    int n_chunks, tiles_per_chunk, BH;
+    int d;
+    // linear branch: prepared state for each (bh, chunk)
+    int phi;                  // Phi
+    int lin_always;           // linear branch active for every chunk (streaming, state nonempty)
+    const void* s_hi;         // bf16 [d][D'] hi part of S^T  (fp32 path: fp32 S^T here, s_lo unused)
+    const void* s_lo;         // bf16 [d][D'] lo part
+    const float* z;           // fp32 [D']
+    long long s_chunk_stride; // elements between consecutive chunks' prepared states
+    long long s_bh_stride;    // elements between consecutive (b,h)
+    long long z_chunk_stride, z_bh_stride;
+    // optional partials (verification aid): fp32
+    float* pm; float* pnt; float* poS; float* poL; float* pnL;
+};
+
+// Block-state pass: partial S^T = sum phi(k) v^T (stored [d][D'] fp32) and
+// z = sum phi(k) over contiguous key sub-blocks of each delta block E_u.
+struct StateParams {
+    const void* k; const void* v;     // [BH][n_rows][d]
+    const void* kp; const void* vp;   // overlap segment (streaming) or null
+    long long bh_stride, prev_bh_stride;
+    int prev_rows;
+    int HW, Tc, To;                   // delta block u covers frames [max(uTc-To,0), max((u+1)Tc-To,0))
+    int n_blocks;                     // U: number of delta blocks
+    int sub_rows;                     // key rows per sub-block
+    int n_sub;                        // sub-blocks per delta block (max over blocks)
+    int stream_rows;                  // streaming: rows of [prev | chunk] to fold (U = 1); 0 in fwd
+    int BH, d, phi;
+    float* partial;                   // [BH][U][n_sub][d*D' + D']
+};
+
+// Scan: X_0 = init (or 0); X_{u+1} = X_u + sum_p partial[u][p].  Writes the
+// prepared form of X_t for t in [t_first, U] and, if state_out, X_U in fp32.
+struct ScanParams {
+    const float* partial;             // [BH][U][n_sub][E]
+    const float* init;                // [BH][E] or null
+    float* state_out;                 // [BH][E] or null (may alias init)
+    void* s_hi; void* s_lo;           // prepared S^T per (bh, t) (bf16 hi/lo, or fp32 in s_hi)
+    float* z;                         // prepared z per (bh, t)
+    long long s_chunk_stride, s_bh_stride, z_chunk_stride, z_bh_stride;
+    int U, n_sub, BH, d, Dp;
+    int t_first;                      // first prepared state to write
+    int t_offset;                     // prepared state X_t is written at slot t - t_offset
+    int f32_prep;                     // prepared form is fp32 (s_hi) rather than bf16 hi/lo
+};
+
+// Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot.
+struct PrevCopyParams {
+    const void* kp; const void* vp; long long prev_bh_stride; int prev_rows;
+    const void* k; const void* v; long long bh_stride; int chunk_rows;
+    void* kd; void* vd;               // destination slot, same stride as prev
+    int keep_rows, BH, d, elem_bytes;
+};
+
+hipError_t launch_local_bf16(const LocalParams& p, hipStream_t s);
+hipError_t launch_local_f32(const LocalParams& p, hipStream_t s);
+hipError_t launch_state_bf16(const StateParams& p, hipStream_t s);
+hipError_t launch_state_f32(const StateParams& p, hipStream_t s);
+hipError_t launch_scan(const ScanParams& p, hipStream_t s);
+hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s);
+
+int local_bf16_tile_rows(int d);   // queries per workgroup of the bf16 local kernel
+int local_f32_tile_rows(int d);
+
+}  // namespace rehyat

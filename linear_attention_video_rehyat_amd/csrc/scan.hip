@@ -1,0 +1,106 @@
+// scan.hip -- cross-chunk carry of the linear state and the overlap-frame copy.
+//
+// The chunk-wise RNN form of ReHyAt (arXiv 2601.04342, §3.3) carries the cached
+// linear sums S = sum phi(k) v^T and z = sum phi(k) (§3.1) from chunk to chunk:
+// chunk t sees X_t = sum_{u<t} E_u, the sums of every delta block that left the
+// softmax window before it.  This kernel forms that exclusive prefix in fp32,
+// sequentially in u (one thread per 4 state elements), and writes each X_t in
+// the form the local kernel's epilogue consumes: S^T split into bf16 hi + lo
+// parts (or fp32 for the fp32 path) and z in fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace rehyat {
+
+namespace {
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
+    const int E = p.d * p.Dp + p.Dp;
+    const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int bh = blockIdx.y;
+    if (e4 >= E) return;
+    const long long pstride = (long long)E;  // between sub-blocks
+    const float* part = p.partial + (long long)bh * p.U * p.n_sub * E + e4;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (p.init) x = *(const f32x4*)(p.init + (long long)bh * E + e4);
+    const int SE = p.d * p.Dp;
+    auto emit = [&](int t) {
+        if (t < p.t_first) return;
+        const int slot = t - p.t_offset;
+        if (e4 < SE) {
+            const long long off = (long long)bh * p.s_bh_stride + (long long)slot * p.s_chunk_stride + e4;
+            if (p.f32_prep) {
+                *(f32x4*)((float*)p.s_hi + off) = x;
+            } else {
+                uint32_t hi[2], lo[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float a = x[2 * j], b = x[2 * j + 1];
+                    const float ha = round_bf16(a), hb = round_bf16(b);
+                    hi[j] = pack2_bf16(ha, hb);
+                    lo[j] = pack2_bf16(a - ha, b - hb);
+                }
+                *(u32x2*)((uint16_t*)p.s_hi + off) = u32x2{hi[0], hi[1]};
+                *(u32x2*)((uint16_t*)p.s_lo + off) = u32x2{lo[0], lo[1]};
+            }
+        } else {
+            const long long off = (long long)bh * p.z_bh_stride + (long long)slot * p.z_chunk_stride + (e4 - SE);
+            *(f32x4*)(p.z + off) = x;
+        }
+    };
+    for (int u = 0; u < p.U; ++u) {
+        emit(u);
+        for (int sp = 0; sp < p.n_sub; ++sp) {
+            const f32x4 d = *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
+            x += d;
+        }
+    }
+    emit(p.U);
+    if (p.state_out) *(f32x4*)(p.state_out + (long long)bh * E + e4) = x;
+}
+
+__global__ __launch_bounds__(256) void prev_copy_kernel(PrevCopyParams p) {
+    // 16-byte chunks of one row: d * elem_bytes / 16
+    const int cpr = p.d * p.elem_bytes / 16;
+    const long long total = (long long)p.BH * p.keep_rows * cpr;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int c = (int)(idx % cpr);
+    const long long rr = idx / cpr;
+    const int r = (int)(rr % p.keep_rows);
+    const int bh = (int)(rr / p.keep_rows);
+    const int j = p.prev_rows + p.chunk_rows - p.keep_rows + r;   // virtual row of [prev | chunk]
+    const char* ks;
+    const char* vs;
+    const long long rowb = (long long)p.d * p.elem_bytes;
+    if (j < p.prev_rows) {
+        ks = (const char*)p.kp + ((long long)bh * p.prev_bh_stride) * p.elem_bytes + j * rowb;
+        vs = (const char*)p.vp + ((long long)bh * p.prev_bh_stride) * p.elem_bytes + j * rowb;
+    } else {
+        ks = (const char*)p.k + ((long long)bh * p.bh_stride) * p.elem_bytes + (j - p.prev_rows) * rowb;
+        vs = (const char*)p.v + ((long long)bh * p.bh_stride) * p.elem_bytes + (j - p.prev_rows) * rowb;
+    }
+    const long long doff = ((long long)bh * p.prev_bh_stride) * p.elem_bytes + r * rowb + 16LL * c;
+    *(u32x4*)((char*)p.kd + doff) = *(const u32x4*)(ks + 16LL * c);
+    *(u32x4*)((char*)p.vd + doff) = *(const u32x4*)(vs + 16LL * c);
+}
+
+}  // namespace
+
+hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
+    const int E = p.d * p.Dp + p.Dp;
+    const int blocks = (E / 4 + 255) / 256;
+    if (blocks <= 0 || p.BH <= 0) return hipSuccess;
+    scan_kernel<<<dim3(blocks, p.BH), 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s) {
+    const long long total = (long long)p.BH * p.keep_rows * (p.d * p.elem_bytes / 16);
+    if (total <= 0) return hipSuccess;
+    const long long blocks = (total + 255) / 256;
+    prev_copy_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace rehyat

@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/rehyat.h, and rejects invalid arguments on the host before
+any GPU work (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_video_rehyat_amd as rh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rehyat.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rh.library_path()),
+                                reason="librehyat.so not built")
+
+EINVAL, EUNSUPPORTED = 1, 2
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rehyat_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = rh.load_library()
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(rh.exported_symbols)
+
+
+def test_status_strings_and_version():
+    lib = rh.load_library()
+    assert lib.rehyat_status_string(0) == b"ok"
+    assert lib.rehyat_status_string(1) == b"invalid argument"
+    assert lib.rehyat_status_string(99) == b"unknown status"
+    assert lib.rehyat_version().startswith(b"librehyat")
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE * 4, B=1, H=1, F=4, HW=8, d=64, Tc=1, To=1, phi=1)
+    a.update(kw)
+    return lib.rehyat_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["B"], a["H"], a["F"], a["HW"],
+                               a["d"], a["Tc"], a["To"], a["phi"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(B=0), EINVAL, "B and H"),
+    (dict(H=-1), EINVAL, "B and H"),
+    (dict(F=0), EINVAL, "frames"),
+    (dict(HW=0), EINVAL, "frames"),
+    (dict(Tc=0), EINVAL, "chunk_frames"),
+    (dict(To=-1), EINVAL, "overlap_frames"),
+    (dict(phi=7), EINVAL, "feature_map"),
+    (dict(d=48), EUNSUPPORTED, "head_dim"),
+    (dict(d=16), EUNSUPPORTED, "head_dim"),
+    (dict(q=0), EINVAL, "null"),
+    (dict(out=0), EINVAL, "null"),
+    (dict(k=FAKE + 2), EINVAL, "aligned"),
+    (dict(out=FAKE), EINVAL, "overlap"),
+    (dict(F=1 << 20, HW=1 << 20), EINVAL, "too large"),
+])
+def test_fwd_validation(kw, code, needle):
+    lib = rh.load_library()
+    assert _fwd(lib, **kw) == code
+    assert needle in lib.rehyat_last_error().decode()
+
+
+def test_f32_head_dims():
+    lib = rh.load_library()
+    st = lib.rehyat_attn_fwd_f32(FAKE, FAKE, FAKE, FAKE * 4, 1, 1, 2, 4, 8, 1, 0, 1, None)
+    assert st == EUNSUPPORTED
+
+
+def test_partials_validation():
+    lib = rh.load_library()
+    st = lib.rehyat_attn_fwd_partials(FAKE, FAKE, FAKE, 1, None, None, None, None, None,
+                                      1, 1, 4, 8, 64, 1, 1, 1, None)
+    assert st == EINVAL and "no partial" in lib.rehyat_last_error().decode()
+    st = lib.rehyat_attn_fwd_partials(FAKE, FAKE, FAKE, 5, FAKE, None, None, None, None,
+                                      1, 1, 4, 8, 64, 1, 1, 1, None)
+    assert st == EINVAL and "dtype" in lib.rehyat_last_error().decode()
+
+
+def test_step_state_bytes_constant_in_video_length():
+    """The streaming state is sized by the chunk geometry alone (constant memory)."""
+    lib = rh.load_library()
+    n = lib.rehyat_step_state_bytes(1, 12, 1560, 128, 3, 1, 1, 1)
+    assert n > 0
+    # holds S (d x D' + D' fp32), prepared hi/lo copies, two overlap slots of T_o frames
+    assert n >= 12 * (128 * 128 + 128) * 4 + 2 * 2 * 12 * 1560 * 128 * 2
+    assert lib.rehyat_step_state_bytes(0, 12, 1560, 128, 3, 1, 1, 1) == 0
+    assert lib.rehyat_step_state_bytes(1, 12, 1560, 100, 3, 1, 1, 1) == 0
+    # POLY2 doubles the feature dimension
+    assert lib.rehyat_step_state_bytes(1, 12, 1560, 128, 3, 1, 2, 1) > n
+
+
+def test_step_state_init_and_step_validation():
+    lib = rh.load_library()
+    st = rh._StepStateC()
+    need = lib.rehyat_step_state_bytes(1, 2, 8, 64, 2, 1, 1, 1)
+    assert lib.rehyat_step_state_init(ctypes.byref(st), FAKE, need - 1, 1, 2, 8, 64, 2, 1, 1, 1) == EINVAL
+    assert "too small" in lib.rehyat_last_error().decode()
+    assert lib.rehyat_step_state_init(ctypes.byref(st), FAKE + 8, need, 1, 2, 8, 64, 2, 1, 1, 1) == EINVAL
+    assert lib.rehyat_step_state_init(ctypes.byref(st), FAKE, need, 1, 2, 8, 64, 2, 1, 1, 1) == 0
+    assert st.frames_done == 0 and st.prev_frames == 0 and st.state_nonempty == 0
+    # frames outside [1, chunk_frames] are rejected before any GPU work
+    assert lib.rehyat_attn_step(ctypes.byref(st), FAKE, FAKE, FAKE, FAKE * 64, 3, None) == EINVAL
+    assert lib.rehyat_attn_step(ctypes.byref(st), FAKE, FAKE, FAKE, FAKE * 64, 0, None) == EINVAL
+    assert lib.rehyat_attn_step(ctypes.byref(st), 0, FAKE, FAKE, FAKE * 64, 1, None) == EINVAL
+    # a stream that ended with a partial chunk takes no more chunks
+    st.frames_done = 3
+    assert lib.rehyat_attn_step(ctypes.byref(st), FAKE, FAKE, FAKE, FAKE * 64, 2, None) == EINVAL
+    assert "partial" in lib.rehyat_last_error().decode()
+    assert lib.rehyat_attn_step(None, FAKE, FAKE, FAKE, FAKE, 1, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(rh.RehyatError):
+        rh.attn_fwd(q, q, q, 1, 8, 1, 0)
