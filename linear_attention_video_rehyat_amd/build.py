@@ -71,6 +71,13 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
+    # a kernel whose host stub was silently dropped leaves an undefined symbol
+    # that only shows up when the library is loaded: refuse to install it
+    nm = subprocess.run(["nm", "-u", "-C", tmp], capture_output=True, text=True)
+    missing = [l.strip() for l in nm.stdout.splitlines() if "__device_stub__" in l or "rehyat::" in l]
+    if missing:
+        os.unlink(tmp)
+        raise RuntimeError("link left undefined kernel symbols:\n" + "\n".join(missing[:10]))
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -62,6 +62,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const lds_u16* base, int elem_offs
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// Row pitch (in 16-bit elements) for a row-major LDS tile of `cols` columns
+// that is read with lds_read_tr: each read covers 8 rows x 64 bytes, so rows
+// should start 16 banks apart (pitch = 64 or 192 bytes mod 256) to spread them
+// over all 64 banks.
+constexpr int tr_pitch(int cols) {
+    int pad = 0;
+    while (((cols + pad) * 2) % 256 != 64 && ((cols + pad) * 2) % 256 != 192) pad += 8;
+    return cols + pad;
+}
+
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }

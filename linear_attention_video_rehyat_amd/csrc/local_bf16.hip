@@ -16,7 +16,11 @@
 // 16 of its keys: row max and row sum need only in-lane work plus one swap
 // between the two 32-lane halves.  P^T then feeds O^T += V^T P^T directly from
 // registers; V^T fragments come from the row-major V tile in LDS through the
-// transposing LDS read.  K/V tiles of BN keys are double-buffered in LDS.
+// transposing LDS read.  K/V tiles of BN keys stream into a ring of LDS stages
+// by direct global->LDS buffer loads (no register staging), issued two tiles
+// ahead; rows are stored unpadded with an XOR swizzle of their 16-byte chunks
+// so that both the K fragment reads and the transposing V reads are free of
+// bank conflicts.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,33 +30,89 @@ namespace {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep a stale max while P <= 2^8
 
+// s_waitcnt immediate with expcnt and lgkmcnt at their maxima and vmcnt = 0;
+// OR in the wanted vmcnt (low 4 bits in [3:0], high 2 bits in [15:14]).
+constexpr unsigned kVmcntBase = 0x0F70;
+
+// XOR swizzle of the 16-byte chunks of row r of an unpadded tile with C chunks
+// per row (C = head_dim / 8).  Chosen so that (a) 16 consecutive rows read at
+// one logical chunk hit 16 different 4-bank groups (K fragment reads), and (b)
+// 4 consecutive rows read at 4 consecutive logical chunks (a transposing V
+// read) land in 4 different 16-bank groups.
+template <int C>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (C == 16) return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (C == 8) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+}
+
+// One wave's share of the direct global->LDS loads of a K/V tile: op o of the
+// wave fills 64 consecutive 16-byte LDS chunk positions of the K tile (ops <
+// NINST) or of the V tile.  Virtual key row j < prev_rows reads the overlap
+// segment, the others read the clip at row j + seg_shift.  Rows past a
+// buffer's end read as zero.
+template <int NW, int OPW, int OPS, int NINST, int KTILE, int BN>
+__device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile_idx, int prev_rows, int seg_shift,
+                                               int rb, const int* op_row, const int* op_c16,
+                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                               __amdgpu_buffer_rsrc_t kprs, __amdgpu_buffer_rsrc_t vprs) {
+#pragma unroll
+    for (int o = 0; o < OPW; ++o) {
+        const int op = wave + o * NW;
+        if (OPS % NW == 0 || op < OPS) {
+            // K or V: decided at compile time when the ops split evenly over the waves
+            const bool isv = NINST % NW == 0 ? o >= NINST / NW : op >= NINST;
+            lds_u16* dst = base + (isv ? KTILE : 0) + 64 * (op % NINST) * 8;
+            const int j = tile_idx * BN + op_row[o];  // virtual key row
+            const int off_prev = j * rb + op_c16[o];
+            const int off_clip = (j + seg_shift) * rb + op_c16[o];
+            auto* lds = (__attribute__((address_space(3))) void*)dst;
+            if (prev_rows == 0) {  // whole-clip forward: one segment, scalar resource
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, lds, 16, off_clip, 0, 0, 0);
+            } else if (isv) {
+                if (j < prev_rows) __builtin_amdgcn_raw_ptr_buffer_load_lds(vprs, lds, 16, off_prev, 0, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds, 16, off_clip, 0, 0, 0);
+            } else {
+                if (j < prev_rows) __builtin_amdgcn_raw_ptr_buffer_load_lds(kprs, lds, 16, off_prev, 0, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds, 16, off_clip, 0, 0, 0);
+            }
+        }
+    }
+}
+
 template <int D, int QB, int NW, int BN, int PHI>
 __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
-    constexpr int PITCH = D + 8;                 // LDS row pitch (elements), 16-byte aligned rows
-    constexpr int TILE = BN * PITCH;
+    constexpr int C = D / 8;                     // 16-byte chunks per row
+    constexpr int KTILE = BN * D;                // elements of one K (or V) tile
+    constexpr int STAGE = 2 * KTILE;             // one K + one V tile
+    constexpr int STAGES = 3;
     constexpr int KS = D / 16;                   // k-steps over head_dim
     constexpr int DT = D / 32;                   // 32-row tiles over head_dim
     constexpr int KT = BN / 32;                  // 32-key tiles per LDS tile
     constexpr int BM = NW * QB * 32;
     constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
     constexpr int KSL = DP / 16;                 // k-steps over the feature dimension
-    constexpr int CHUNKS = BN * D / 8;           // 16-byte chunks per K (or V) tile
-    constexpr int CPT = (CHUNKS + NW * 64 - 1) / (NW * 64);
+    constexpr int NINST = BN * C / 64;           // 64-lane DMA instructions per K (or V) tile
+    constexpr int OPS = 2 * NINST;               // per tile, K and V
+    constexpr int OPW = (OPS + NW - 1) / NW;     // per wave
+    static_assert(NINST >= 1, "tile too small");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem_raw[4 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem_raw[STAGES * STAGE];
     lds_u16* smem = (lds_u16*)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int h = lane >> 5;
     const int lq = lane & 31;
 
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    // block -> (bh, chunk, query tile); integer division is expanded on the
+    // vector ALU, so pin the (uniform) results to scalar registers
+    const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
     const int per_bh = p.n_chunks * p.tiles_per_chunk;
-    const int bh = item / per_bh;
+    const int bh = __builtin_amdgcn_readfirstlane(item / per_bh);
     const int rem = item - bh * per_bh;
-    const int t = rem / p.tiles_per_chunk;
+    const int t = __builtin_amdgcn_readfirstlane(rem / p.tiles_per_chunk);
     const int tile = rem - t * p.tiles_per_chunk;
     const int f0 = t * p.Tc;
     const int f1 = min(f0 + p.Tc, p.F);
@@ -79,43 +139,30 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         for (int ks = 0; ks < KS; ++ks) qreg[qb][ks] = __builtin_bit_cast(bf16x8, ldg_b128(src + 16 * ks));
     }
 
-    // ---- K/V tile staging: global -> registers -> LDS
-    u32x4 kst[CPT], vst[CPT];
-    auto load_tile = [&](int it) {
+    // ---- K/V tiles: direct global->LDS loads into a ring of STAGES stages.
+    // Instruction i of a tile covers physical 16-byte chunk positions
+    // 64i .. 64i+63 (1 KB of LDS); lane l fills position P = 64i + l, i.e. row
+    // P / C, physical chunk P % C, which holds logical chunk (P % C) ^ swz(row).
+    const int rb = D * 2;  // row bytes
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kb_ptr), (short)0, q_end * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vb_ptr), (short)0, q_end * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kp_ptr ? kp_ptr : kb_ptr), (short)0, p.prev_rows * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vp_ptr ? vp_ptr : vb_ptr), (short)0, p.prev_rows * rb, 0x00020000);
+    int op_row[OPW], op_c16[OPW];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NW * 64;
-            if (CHUNKS % (NW * 64) == 0 || c < CHUNKS) {
-                const int r = c / (D / 8);
-                const int col = (c % (D / 8)) * 8;
-                const int j = min(it * BN + r, nkeys - 1);
-                const uint16_t* ks_;
-                const uint16_t* vs_;
-                if (j < p.prev_rows) {
-                    ks_ = kp_ptr + (long long)j * D + col;
-                    vs_ = vp_ptr + (long long)j * D + col;
-                } else {
-                    ks_ = kb_ptr + (long long)(j + seg_shift) * D + col;
-                    vs_ = vb_ptr + (long long)(j + seg_shift) * D + col;
-                }
-                kst[i] = ldg_b128(ks_);
-                vst[i] = ldg_b128(vs_);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        lds_u16* Kd = smem + buf * 2 * TILE;
-        lds_u16* Vd = Kd + TILE;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NW * 64;
-            if (CHUNKS % (NW * 64) == 0 || c < CHUNKS) {
-                const int r = c / (D / 8);
-                const int col = (c % (D / 8)) * 8;
-                lds_write_b128(Kd, r * PITCH + col, kst[i]);
-                lds_write_b128(Vd, r * PITCH + col, vst[i]);
-            }
-        }
+    for (int o = 0; o < OPW; ++o) {
+        const int op = wave + o * NW;
+        const int pos = 64 * (op % NINST) + lane;
+        op_row[o] = pos / C;
+        op_c16[o] = ((pos % C) ^ swz<C>(pos / C)) * 16;
+    }
+    auto issue_tile = [&](int tile_idx, int stage) {
+        issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(smem + stage * STAGE, wave, tile_idx, p.prev_rows, seg_shift,
+                                                       rb, op_row, op_c16, krs, vrs, kprs, vprs);
     };
 
     f32x16 oacc[QB][DT];
@@ -129,22 +176,32 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         mtrue[qb] = -INFINITY;
     }
 
-    const int ntiles = (nkeys + BN - 1) / BN;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    // V^T fragment addressing for the transposing read (see lds_read_tr)
+    // V^T fragment addressing for the transposing read (see lds_read_tr):
+    // logical row 4h + (lane%16)/4 (+8), column 16*((lane/16)%2) + 4*(lane%4)
     const int tr_row = 4 * h + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // within a 32-column tile
+    const int tr_sub = 4 * (lane & 1);                                // element offset in the chunk
 
+    const int ntiles = (nkeys + BN - 1) / BN;
+    issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
+    int stage = 0;
     for (int it = 0; it < ntiles; ++it) {
-        const int cur = it & 1;
-        if (it + 1 < ntiles) load_tile(it + 1);
-        const lds_u16* Ks = smem + cur * 2 * TILE;
-        const lds_u16* Vs = Ks + TILE;
+        // own loads of tile `it` have landed (tile it+1 may still be in flight),
+        // then every wave's have, and every wave is done with tile it-1
+        if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kVmcntBase | (OPW & 15) | ((OPW >> 4) << 14));
+        else __builtin_amdgcn_s_waitcnt(kVmcntBase);
+        // plain s_barrier: __syncthreads() would also wait for the DMA of tile
+        // it+1; the compiler-only fences keep LDS accesses on their side of it
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (it + 2 < ntiles) issue_tile(it + 2, stage == 0 ? 2 : stage - 1);
+        const lds_u16* Ks = smem + stage * STAGE;
+        const lds_u16* Vs = Ks + KTILE;
+        stage = stage == STAGES - 1 ? 0 : stage + 1;
 
-        // S^T = K Q^T: lane holds query lq of each block, keys (r/4)*8 + 4h + r%4
+        // S^T = K Q^T: lane holds query lq of each block, keys 32kt + (r/4)*8 + 4h + r%4
         f32x16 sacc[QB][KT];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -154,7 +211,8 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const bf16x8 a = lds_read_b128(Ks, (32 * kt + lq) * PITCH + 16 * ks + 8 * h);
+                const int row = 32 * kt + lq;
+                const bf16x8 a = lds_read_b128(Ks, row * D + (((2 * ks + h) ^ swz<C>(row)) << 3));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) sacc[qb][kt] = mfma32x32x16(a, qreg[qb][ks], sacc[qb][kt]);
             }
@@ -227,18 +285,16 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
-                const int row = 32 * kt + 16 * sp + tr_row;
+                const int r0 = 32 * kt + 16 * sp + tr_row, r1 = r0 + 8;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const int col = 32 * dt + tr_col;
-                    const bf16x8 a = cat(lds_read_tr(Vs, row * PITCH + col), lds_read_tr(Vs, (row + 8) * PITCH + col));
+                    const int c = 4 * dt + tr_chunk;
+                    const bf16x8 a = cat(lds_read_tr(Vs, r0 * D + ((c ^ swz<C>(r0)) << 3) + tr_sub),
+                                         lds_read_tr(Vs, r1 * D + ((c ^ swz<C>(r1)) << 3) + tr_sub));
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32x32x16(a, pfrag[qb][kt][sp], oacc[qb][dt]);
                 }
             }
-
-        if (it + 1 < ntiles) store_tile(cur ^ 1);
-        __syncthreads();
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -367,8 +423,18 @@ hipError_t launch_d(const LocalParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Tile configuration: QB query blocks of 32 per wave, NW waves, BN keys per LDS tile.
-constexpr int kQB = 2, kNW = 4, kBN = 32;
+// Tile configuration: QB query blocks of 32 per wave, NW waves, BN keys per LDS
+// tile (overridable at build time for tuning sweeps).
+#ifndef REHYAT_LOCAL_QB
+#define REHYAT_LOCAL_QB 1
+#endif
+#ifndef REHYAT_LOCAL_NW
+#define REHYAT_LOCAL_NW 8
+#endif
+#ifndef REHYAT_LOCAL_BN
+#define REHYAT_LOCAL_BN 64
+#endif
+constexpr int kQB = REHYAT_LOCAL_QB, kNW = REHYAT_LOCAL_NW, kBN = REHYAT_LOCAL_BN;
 
 }  // namespace
 

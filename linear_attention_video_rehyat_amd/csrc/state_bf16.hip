@@ -25,8 +25,8 @@ __global__ __launch_bounds__(256) void state_bf16_kernel(StateParams p) {
     constexpr int NW = 4;
     constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
     constexpr int BN = 32;                        // keys per LDS tile
-    constexpr int VP = D + 8;                     // pitches (elements)
-    constexpr int FP = DP + 8;
+    constexpr int VP = tr_pitch(D);               // pitches (elements) for transposing reads
+    constexpr int FP = tr_pitch(DP);
     constexpr int VT = BN * VP, FT = BN * FP;
     constexpr int BUF = VT + 2 * FT;              // one buffer: V, phi_hi, phi_lo
     constexpr int DT = D / 32, NT = DP / 32;
