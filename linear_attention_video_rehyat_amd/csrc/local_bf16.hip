@@ -33,6 +33,7 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep a stale max while
 // s_waitcnt immediate with expcnt and lgkmcnt at their maxima and vmcnt = 0;
 // OR in the wanted vmcnt (low 4 bits in [3:0], high 2 bits in [15:14]).
 constexpr unsigned kVmcntBase = 0x0F70;
+constexpr unsigned vm_wait_imm(int n) { return kVmcntBase | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
 
 // XOR swizzle of the 16-byte chunks of row r of an unpadded tile with C chunks
 // per row (C = head_dim / 8).  Chosen so that (a) 16 consecutive rows read at
@@ -80,12 +81,13 @@ __device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile
     }
 }
 
-template <int D, int QB, int NW, int BN, int PHI>
+template <int D, int QB, int NW, int BN, int PHI, int LSTAGES>
 __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     constexpr int C = D / 8;                     // 16-byte chunks per row
     constexpr int KTILE = BN * D;                // elements of one K (or V) tile
     constexpr int STAGE = 2 * KTILE;             // one K + one V tile
-    constexpr int STAGES = 3;
+    constexpr int STAGES = LSTAGES;              // LDS ring; tiles are loaded STAGES-1 ahead
+    static_assert(STAGES >= 2 && STAGES <= 4, "2..4 LDS stages");
     constexpr int KS = D / 16;                   // k-steps over head_dim
     constexpr int DT = D / 32;                   // 32-row tiles over head_dim
     constexpr int KT = BN / 32;                  // 32-key tiles per LDS tile
@@ -183,20 +185,23 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     const int tr_sub = 4 * (lane & 1);                                // element offset in the chunk
 
     const int ntiles = (nkeys + BN - 1) / BN;
-    issue_tile(0, 0);
-    if (ntiles > 1) issue_tile(1, 1);
+    constexpr int PF = STAGES - 1;  // tiles in flight ahead of the one being read
+    for (int tt = 0; tt < PF && tt < ntiles; ++tt) issue_tile(tt, tt);
     int stage = 0;
     for (int it = 0; it < ntiles; ++it) {
-        // own loads of tile `it` have landed (tile it+1 may still be in flight),
-        // then every wave's have, and every wave is done with tile it-1
-        if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kVmcntBase | (OPW & 15) | ((OPW >> 4) << 14));
-        else __builtin_amdgcn_s_waitcnt(kVmcntBase);
-        // plain s_barrier: __syncthreads() would also wait for the DMA of tile
-        // it+1; the compiler-only fences keep LDS accesses on their side of it
+        // own loads of tile `it` have landed (tiles it+1 .. it+PF-1 may still be
+        // in flight), then every wave's have, and every wave is done with tile it-1
+        const int ahead = min(PF - 1, ntiles - 1 - it);
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
+        else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        // plain s_barrier: __syncthreads() would also drain the prefetch; the
+        // compiler-only fences keep LDS accesses on their side of it
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (it + 2 < ntiles) issue_tile(it + 2, stage == 0 ? 2 : stage - 1);
+        // the slot of tile it-1 is free: refill it with tile it+PF
+        if (it + PF < ntiles) issue_tile(it + PF, stage == 0 ? STAGES - 1 : stage - 1);
         const lds_u16* Ks = smem + stage * STAGE;
         const lds_u16* Vs = Ks + KTILE;
         stage = stage == STAGES - 1 ? 0 : stage + 1;
@@ -409,20 +414,6 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     }
 }
 
-template <int D, int QB, int NW, int BN>
-hipError_t launch_d(const LocalParams& p, hipStream_t s) {
-    const int blocks = p.BH * p.n_chunks * p.tiles_per_chunk;
-    if (blocks <= 0) return hipSuccess;
-    dim3 grid(blocks), block(NW * 64);
-    switch (p.phi) {
-    case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone><<<grid, block, 0, s>>>(p); break;
-    case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1><<<grid, block, 0, s>>>(p); break;
-    case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2><<<grid, block, 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
 // Tile configuration: QB query blocks of 32 per wave, NW waves, BN keys per LDS
 // tile (overridable at build time for tuning sweeps).
 #ifndef REHYAT_LOCAL_QB
@@ -434,7 +425,25 @@ hipError_t launch_d(const LocalParams& p, hipStream_t s) {
 #ifndef REHYAT_LOCAL_BN
 #define REHYAT_LOCAL_BN 64
 #endif
-constexpr int kQB = REHYAT_LOCAL_QB, kNW = REHYAT_LOCAL_NW, kBN = REHYAT_LOCAL_BN;
+#ifndef REHYAT_LOCAL_STAGES
+#define REHYAT_LOCAL_STAGES 3
+#endif
+constexpr int kQB = REHYAT_LOCAL_QB, kNW = REHYAT_LOCAL_NW, kBN = REHYAT_LOCAL_BN, kStages = REHYAT_LOCAL_STAGES;
+
+template <int D, int QB, int NW, int BN>
+hipError_t launch_d(const LocalParams& p, hipStream_t s) {
+    const int blocks = p.BH * p.n_chunks * p.tiles_per_chunk;
+    if (blocks <= 0) return hipSuccess;
+    dim3 grid(blocks), block(NW * 64);
+    switch (p.phi) {
+    case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone, kStages><<<grid, block, 0, s>>>(p); break;
+    case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1, kStages><<<grid, block, 0, s>>>(p); break;
+    case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2, kStages><<<grid, block, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 
 }  // namespace
 
