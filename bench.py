@@ -31,10 +31,23 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-# HBM bytes per dispatch of the local-softmax kernel from rocprofv3 FETCH_SIZE +
-# WRITE_SIZE, scaled by the copy-kernel calibration; None until measured for the
-# current kernel.
-LOCAL_KERNEL_TRAFFIC_BYTES = None
+# HBM bytes per dispatch of the local-softmax kernel at the default workload, from
+# rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
+# gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
+# it was measured on: reported as null once local_bf16.hip changes.
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "929812a8ca55ce85", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (246500 * 2.0 + 98280 * 1.0) * 1024}
+
+
+def local_kernel_traffic(workload, phi, chunk_frames):
+    import hashlib
+    src = os.path.join(ROOT, "linear_attention_video_rehyat_amd", "csrc", "local_bf16.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    t = LOCAL_KERNEL_TRAFFIC
+    if (sha, workload, phi, chunk_frames) != (t["source_sha256_16"], t["workload"], t["phi"], t["chunk_frames"]):
+        return None
+    return t["bytes"]
 
 
 class Hip:
@@ -197,7 +210,7 @@ def main():
     local_tflops = cnt["softmax_flops"] / (main_t["local_ms"] / 1000.0) / 1e12
     roofline = {"bound": "mfma", "achieved": round(local_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(local_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": LOCAL_KERNEL_TRAFFIC_BYTES, "kernel": "local_bf16_kernel",
+                "traffic": local_kernel_traffic(w.name, phi, Tc), "kernel": "local_bf16_kernel",
                 "ms": round(main_t["local_ms"], 4),
                 "algorithmic_flops": cnt["softmax_flops"]}
     state = None
