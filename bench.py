@@ -35,8 +35,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "929812a8ca55ce85", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (246500 * 2.0 + 98280 * 1.0) * 1024}
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "7b0620a093beb46d", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (246849 * 2.0 + 98280 * 1.0) * 1024}
 
 
 def local_kernel_traffic(workload, phi, chunk_frames):

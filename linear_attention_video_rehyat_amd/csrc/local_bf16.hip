@@ -81,7 +81,7 @@ __device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile
     }
 }
 
-template <int D, int QB, int NW, int BN, int PHI, int LSTAGES>
+template <int D, int QB, int NW, int BN, int PHI, int LSTAGES, bool SKEW>
 __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     constexpr int C = D / 8;                     // 16-byte chunks per row
     constexpr int KTILE = BN * D;                // elements of one K (or V) tile
@@ -185,28 +185,42 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     const int tr_sub = 4 * (lane & 1);                                // element offset in the chunk
 
     const int ntiles = (nkeys + BN - 1) / BN;
-    constexpr int PF = STAGES - 1;  // tiles in flight ahead of the one being read
+    // Skewed schedule: waves NW/2 .. NW-1 (the second wave of every SIMD) run
+    // the PV product of the previous tile before the scores of the current
+    // one, so the two waves of a SIMD are in different phases (one in MFMA
+    // work while the other runs its softmax) between the same barriers.  Their
+    // V tile stays in LDS one iteration longer: loads run PF = STAGES-2 ahead.
+    constexpr int PF = SKEW ? STAGES - 2 : STAGES - 1;
+    static_assert(PF >= 1, "not enough LDS stages");
+    const bool late = SKEW && wave >= NW / 2;
     for (int tt = 0; tt < PF && tt < ntiles; ++tt) issue_tile(tt, tt);
-    int stage = 0;
-    for (int it = 0; it < ntiles; ++it) {
-        // own loads of tile `it` have landed (tiles it+1 .. it+PF-1 may still be
-        // in flight), then every wave's have, and every wave is done with tile it-1
-        const int ahead = min(PF - 1, ntiles - 1 - it);
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
-        else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-        // plain s_barrier: __syncthreads() would also drain the prefetch; the
-        // compiler-only fences keep LDS accesses on their side of it
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        // the slot of tile it-1 is free: refill it with tile it+PF
-        if (it + PF < ntiles) issue_tile(it + PF, stage == 0 ? STAGES - 1 : stage - 1);
-        const lds_u16* Ks = smem + stage * STAGE;
-        const lds_u16* Vs = Ks + KTILE;
-        stage = stage == STAGES - 1 ? 0 : stage + 1;
+    auto kslot = [&](int i) -> const lds_u16* { return smem + (i % STAGES) * STAGE; };
+    auto vslot = [&](int i) -> const lds_u16* { return smem + (i % STAGES) * STAGE + KTILE; };
 
-        // S^T = K Q^T: lane holds query lq of each block, keys 32kt + (r/4)*8 + 4h + r%4
+    bf16x8 pfrag[QB][KT][2];
+    // O^T += V^T(tile) P^T
+    auto pv = [&](int tile_idx) {
+        const lds_u16* Vs = vslot(tile_idx);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const int r0 = 32 * kt + 16 * sp + tr_row, r1 = r0 + 8;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int c = 4 * dt + tr_chunk;
+                    const bf16x8 a = cat(lds_read_tr(Vs, r0 * D + ((c ^ swz<C>(r0)) << 3) + tr_sub),
+                                         lds_read_tr(Vs, r1 * D + ((c ^ swz<C>(r1)) << 3) + tr_sub));
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32x32x16(a, pfrag[qb][kt][sp], oacc[qb][dt]);
+                }
+            }
+    };
+    // S^T(tile) = K Q^T (lane holds query lq, keys 32kt + (r/4)*8 + 4h + r%4),
+    // then the online softmax -> P(tile), log2 domain; the running max is only
+    // moved when a new score exceeds it by more than kRescaleThreshold
+    auto scores_softmax = [&](int it) {
+        const lds_u16* Ks = kslot(it);
         f32x16 sacc[QB][KT];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -222,9 +236,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
                 for (int qb = 0; qb < QB; ++qb) sacc[qb][kt] = mfma32x32x16(a, qreg[qb][ks], sacc[qb][kt]);
             }
         }
-
-        // keys past the window end (last tile only)
-        if ((it + 1) * BN > nkeys) {
+        if ((it + 1) * BN > nkeys) {  // keys past the window end (last tile only)
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -236,9 +248,6 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
                     }
                 }
         }
-
-        // online softmax, log2 domain; the running max is only moved when a
-        // new score exceeds it by more than kRescaleThreshold
         float mt[QB];
         bool need = false;
 #pragma unroll
@@ -264,7 +273,6 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
                 m2[qb] = mn;
             }
         }
-        bf16x8 pfrag[QB][KT][2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float negm = -m2[qb];
@@ -284,23 +292,33 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
                     pfrag[qb][kt][sp] = __builtin_bit_cast(bf16x8, w);
                 }
         }
+    };
 
-        // O^T += V^T P^T
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-                const int r0 = 32 * kt + 16 * sp + tr_row, r1 = r0 + 8;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int c = 4 * dt + tr_chunk;
-                    const bf16x8 a = cat(lds_read_tr(Vs, r0 * D + ((c ^ swz<C>(r0)) << 3) + tr_sub),
-                                         lds_read_tr(Vs, r1 * D + ((c ^ swz<C>(r1)) << 3) + tr_sub));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32x32x16(a, pfrag[qb][kt][sp], oacc[qb][dt]);
-                }
-            }
+    for (int it = 0; it < ntiles; ++it) {
+        // own loads of tile `it` have landed (tiles it+1 .. it+PF-1 may still be
+        // in flight), then every wave's have, and every wave is done with the
+        // slot refilled next
+        const int ahead = min(PF - 1, ntiles - 1 - it);
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
+        else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        // plain s_barrier: __syncthreads() would also drain the prefetch; the
+        // compiler-only fences keep LDS accesses on their side of it
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // refill the slot last read in the previous iteration (lockstep: tile
+        // it-1; skewed: tile it-2, whose V the late waves read at it-1)
+        if (it + PF < ntiles) issue_tile(it + PF, (it + PF) % STAGES);
+        if (late) {
+            if (it > 0) pv(it - 1);
+            scores_softmax(it);
+        } else {
+            scores_softmax(it);
+            pv(it);
+        }
     }
+    if (late && ntiles > 0) pv(ntiles - 1);
 
     // ---------------------------------------------------------------- epilogue
     const bool lin = PHI != kPhiNone && (p.lin_always || w0 > 0);
@@ -423,12 +441,16 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
 #define REHYAT_LOCAL_NW 8
 #endif
 #ifndef REHYAT_LOCAL_BN
-#define REHYAT_LOCAL_BN 64
+#define REHYAT_LOCAL_BN 128
 #endif
 #ifndef REHYAT_LOCAL_STAGES
-#define REHYAT_LOCAL_STAGES 3
+#define REHYAT_LOCAL_STAGES 2
+#endif
+#ifndef REHYAT_LOCAL_SKEW
+#define REHYAT_LOCAL_SKEW 0
 #endif
 constexpr int kQB = REHYAT_LOCAL_QB, kNW = REHYAT_LOCAL_NW, kBN = REHYAT_LOCAL_BN, kStages = REHYAT_LOCAL_STAGES;
+constexpr bool kSkew = REHYAT_LOCAL_SKEW != 0;
 
 template <int D, int QB, int NW, int BN>
 hipError_t launch_d(const LocalParams& p, hipStream_t s) {
@@ -436,9 +458,9 @@ hipError_t launch_d(const LocalParams& p, hipStream_t s) {
     if (blocks <= 0) return hipSuccess;
     dim3 grid(blocks), block(NW * 64);
     switch (p.phi) {
-    case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone, kStages><<<grid, block, 0, s>>>(p); break;
-    case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1, kStages><<<grid, block, 0, s>>>(p); break;
-    case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2, kStages><<<grid, block, 0, s>>>(p); break;
+    case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone, kStages, kSkew><<<grid, block, 0, s>>>(p); break;
+    case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1, kStages, kSkew><<<grid, block, 0, s>>>(p); break;
+    case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2, kStages, kSkew><<<grid, block, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
