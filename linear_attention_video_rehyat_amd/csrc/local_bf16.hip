@@ -21,31 +21,11 @@
 // ahead; rows are stored unpadded with an XOR swizzle of their 16-byte chunks
 // so that both the K fragment reads and the transposing V reads are free of
 // bank conflicts.
-#include "common.h"
-#include "kernels.h"
+#include "local_common.h"
 
 namespace rehyat {
 
 namespace {
-
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep a stale max while P <= 2^8
-
-// s_waitcnt immediate with expcnt and lgkmcnt at their maxima and vmcnt = 0;
-// OR in the wanted vmcnt (low 4 bits in [3:0], high 2 bits in [15:14]).
-constexpr unsigned kVmcntBase = 0x0F70;
-constexpr unsigned vm_wait_imm(int n) { return kVmcntBase | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
-
-// XOR swizzle of the 16-byte chunks of row r of an unpadded tile with C chunks
-// per row (C = head_dim / 8).  Chosen so that (a) 16 consecutive rows read at
-// one logical chunk hit 16 different 4-bank groups (K fragment reads), and (b)
-// 4 consecutive rows read at 4 consecutive logical chunks (a transposing V
-// read) land in 4 different 16-bank groups.
-template <int C>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (C == 16) return 4 * (r & 3) + ((r >> 2) & 3);
-    else if constexpr (C == 8) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-    else return (r >> 2) & 3;
-}
 
 // One wave's share of the direct global->LDS loads of a K/V tile: op o of the
 // wave fills 64 consecutive 16-byte LDS chunk positions of the K tile (ops <
@@ -81,7 +61,7 @@ __device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile
     }
 }
 
-template <int D, int QB, int NW, int BN, int PHI, int LSTAGES, bool SKEW>
+template <int D, int QB, int NW, int BN, int PHI, int LSTAGES>
 __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     constexpr int C = D / 8;                     // 16-byte chunks per row
     constexpr int KTILE = BN * D;                // elements of one K (or V) tile
@@ -183,34 +163,34 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     const int tr_row = 4 * h + ((lane & 15) >> 2);
     const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // within a 32-column tile
     const int tr_sub = 4 * (lane & 1);                                // element offset in the chunk
+    // Lane-dependent parts of the fragment addresses.  The swizzle depends on
+    // the row index mod 16 only, so the 16- and 32-row steps between fragments
+    // become immediate offsets of the LDS reads.
+    int voff[DT][2], koff[KS];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const int c = 4 * dt + tr_chunk;
+        voff[dt][0] = tr_row * D + ((c ^ swz<C>(tr_row)) << 3) + tr_sub;
+        voff[dt][1] = (tr_row + 8) * D + ((c ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = lq * D + (((2 * ks + h) ^ swz<C>(lq)) << 3);
 
     const int ntiles = (nkeys + BN - 1) / BN;
-    // Skewed schedule: waves NW/2 .. NW-1 (the second wave of every SIMD) run
-    // the PV product of the previous tile before the scores of the current
-    // one, so the two waves of a SIMD are in different phases (one in MFMA
-    // work while the other runs its softmax) between the same barriers.  Their
-    // V tile stays in LDS one iteration longer: loads run PF = STAGES-2 ahead.
-    constexpr int PF = SKEW ? STAGES - 2 : STAGES - 1;
-    static_assert(PF >= 1, "not enough LDS stages");
-    const bool late = SKEW && wave >= NW / 2;
+    constexpr int PF = STAGES - 1;  // tiles loaded ahead
     for (int tt = 0; tt < PF && tt < ntiles; ++tt) issue_tile(tt, tt);
-    auto kslot = [&](int i) -> const lds_u16* { return smem + (i % STAGES) * STAGE; };
-    auto vslot = [&](int i) -> const lds_u16* { return smem + (i % STAGES) * STAGE + KTILE; };
 
     bf16x8 pfrag[QB][KT][2];
     // O^T += V^T(tile) P^T
-    auto pv = [&](int tile_idx) {
-        const lds_u16* Vs = vslot(tile_idx);
+    auto pv = [&](const lds_u16* Vs) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
-                const int r0 = 32 * kt + 16 * sp + tr_row, r1 = r0 + 8;
+                const int r = (32 * kt + 16 * sp) * D;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const int c = 4 * dt + tr_chunk;
-                    const bf16x8 a = cat(lds_read_tr(Vs, r0 * D + ((c ^ swz<C>(r0)) << 3) + tr_sub),
-                                         lds_read_tr(Vs, r1 * D + ((c ^ swz<C>(r1)) << 3) + tr_sub));
+                    const bf16x8 a = cat(lds_read_tr(Vs, r + voff[dt][0]), lds_read_tr(Vs, r + voff[dt][1]));
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32x32x16(a, pfrag[qb][kt][sp], oacc[qb][dt]);
                 }
@@ -219,8 +199,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     // S^T(tile) = K Q^T (lane holds query lq, keys 32kt + (r/4)*8 + 4h + r%4),
     // then the online softmax -> P(tile), log2 domain; the running max is only
     // moved when a new score exceeds it by more than kRescaleThreshold
-    auto scores_softmax = [&](int it) {
-        const lds_u16* Ks = kslot(it);
+    auto scores_softmax = [&](int it, const lds_u16* Ks) {
         f32x16 sacc[QB][KT];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -230,11 +209,22 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int row = 32 * kt + lq;
-                const bf16x8 a = lds_read_b128(Ks, row * D + (((2 * ks + h) ^ swz<C>(row)) << 3));
+                const bf16x8 a = lds_read_b128(Ks, 32 * kt * D + koff[ks]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) sacc[qb][kt] = mfma32x32x16(a, qreg[qb][ks], sacc[qb][kt]);
             }
+        }
+        // scheduling hint: keep up to 8 K-fragment reads in flight ahead of the
+        // MFMAs that consume them (LDS latency is otherwise exposed per pair)
+        {
+            constexpr int NR = KS * KT, AH = NR < 8 ? NR : 8;
+            __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // DS reads
+#pragma unroll
+            for (int i = 0; i < NR - AH; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, QB * AH, 0);
         }
         if ((it + 1) * BN > nkeys) {  // keys past the window end (last tile only)
 #pragma unroll
@@ -294,6 +284,18 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         }
     };
 
+    // One iteration: refill the slot read in the previous iteration, then
+    // scores, softmax and PV of tile `it`.  The slot being filled and the slot
+    // being read are passed as restrict pointers: they never overlap, and the
+    // compiler may then keep the transposing V reads clear of the wait for the
+    // loads still in flight (it cannot otherwise tell them apart).
+    auto iteration = [&](int it, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
+        if (it + PF < ntiles)
+            issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(fill, wave, it + PF, p.prev_rows, seg_shift, rb, op_row,
+                                                           op_c16, krs, vrs, kprs, vprs);
+        scores_softmax(it, cur);
+        pv(cur + KTILE);
+    };
     for (int it = 0; it < ntiles; ++it) {
         // own loads of tile `it` have landed (tiles it+1 .. it+PF-1 may still be
         // in flight), then every wave's have, and every wave is done with the
@@ -302,134 +304,16 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
         else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
         else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-        // plain s_barrier: __syncthreads() would also drain the prefetch; the
-        // compiler-only fences keep LDS accesses on their side of it
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        // refill the slot last read in the previous iteration (lockstep: tile
-        // it-1; skewed: tile it-2, whose V the late waves read at it-1)
-        if (it + PF < ntiles) issue_tile(it + PF, (it + PF) % STAGES);
-        if (late) {
-            if (it > 0) pv(it - 1);
-            scores_softmax(it);
-        } else {
-            scores_softmax(it);
-            pv(it);
-        }
+        lds_barrier();
+        iteration(it, smem + ((it + PF) % STAGES) * STAGE, smem + (it % STAGES) * STAGE);
     }
-    if (late && ntiles > 0) pv(ntiles - 1);
 
     // ---------------------------------------------------------------- epilogue
     const bool lin = PHI != kPhiNone && (p.lin_always || w0 > 0);
-    const uint16_t* shi = nullptr;
-    const uint16_t* slo = nullptr;
-    const float* zp = nullptr;
-    if (lin) {
-        shi = (const uint16_t*)p.s_hi + bh * p.s_bh_stride + t * p.s_chunk_stride;
-        slo = (const uint16_t*)p.s_lo + bh * p.s_bh_stride + t * p.s_chunk_stride;
-        zp = p.z + bh * p.z_bh_stride + t * p.z_chunk_stride;
-    }
-    uint16_t* ob_ptr = (uint16_t*)p.out + bh * p.bh_stride;
-
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float lsum = xhalf_sum(msum[qb]);
-        f32x16 lacc[DT];
-        float nl = 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) lacc[dt] = f32x16{};
-        if (PHI != kPhiNone && lin) {
-            // a^L^T = S_t^T phi(Q)^T with a three-pass bf16 split of both operands;
-            // n^L = phi(q).z in fp32
-            float nlp = 0.0f;
-#pragma unroll
-            for (int ksl = 0; ksl < KSL; ++ksl) {
-                float x[8];
-                unpack8(__builtin_bit_cast(u32x4, qreg[qb][ksl % KS]), x);
-                float f[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) f[j] = ksl < KS ? elu1(x[j]) : x[j] * x[j];
-                const f32x4 z0 = *(const f32x4*)(zp + 16 * ksl + 8 * h);
-                const f32x4 z1 = *(const f32x4*)(zp + 16 * ksl + 8 * h + 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) nlp += f[j] * z0[j] + f[4 + j] * z1[j];
-                u32x4 whi, wlo;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float h0 = round_bf16(f[2 * j]), h1 = round_bf16(f[2 * j + 1]);
-                    whi[j] = pack2_bf16(h0, h1);
-                    wlo[j] = pack2_bf16(f[2 * j] - h0, f[2 * j + 1] - h1);
-                }
-                const bf16x8 fhi = __builtin_bit_cast(bf16x8, whi);
-                const bf16x8 flo = __builtin_bit_cast(bf16x8, wlo);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
-                    const bf16x8 ahi = __builtin_bit_cast(bf16x8, ldg_b128(shi + off));
-                    const bf16x8 alo = __builtin_bit_cast(bf16x8, ldg_b128(slo + off));
-                    lacc[dt] = mfma32x32x16(ahi, fhi, lacc[dt]);
-                    lacc[dt] = mfma32x32x16(alo, fhi, lacc[dt]);
-                    lacc[dt] = mfma32x32x16(ahi, flo, lacc[dt]);
-                }
-            }
-            nl = xhalf_sum(nlp);
-        }
-        // joint normalisation, shifted by M2 = max(m2, log2 n^L)
-        float cs = 1.0f, cl = 0.0f;
-        if (PHI != kPhiNone && lin && nl > 0.0f) {
-            const float M2 = fmaxf(m2[qb], __builtin_amdgcn_logf(nl));
-            cs = __builtin_amdgcn_exp2f(m2[qb] - M2);
-            cl = __builtin_amdgcn_exp2f(-M2);
-        }
-        const float inv = 1.0f / (cs * lsum + cl * nl);
-
-        const int row = q_start + (wave * QB + qb) * 32 + lq;
-        const bool valid = row < q_end;
-        if (!valid) {
-            // rows past the chunk end hold duplicated queries; nothing to store
-        } else if (p.pm == nullptr && p.poS == nullptr && p.poL == nullptr && p.pnt == nullptr && p.pnL == nullptr) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float y[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float num = PHI != kPhiNone ? cs * oacc[qb][dt][4 * g + j] + cl * lacc[dt][4 * g + j]
-                                                          : oacc[qb][dt][4 * g + j];
-                        y[j] = num * inv;
-                    }
-                    u32x2 w = {pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
-                    *(u32x2*)(ob_ptr + (long long)row * D + 32 * dt + 8 * g + 4 * h) = w;
-                }
-        } else {
-            const long long prow = bh * (long long)(p.bh_stride / D) + row;
-            if (h == 0) {
-                if (p.pm) p.pm[prow] = mtrue[qb];
-                if (p.pnt) p.pnt[prow] = lsum * __builtin_amdgcn_exp2f(m2[qb] - mtrue[qb] * kLog2e);
-                if (p.pnL) p.pnL[prow] = nl;
-            }
-            const float invl = 1.0f / lsum;
-            const float invn = nl > 0.0f ? 1.0f / nl : 0.0f;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = 32 * dt + 8 * g + 4 * h;
-                    if (p.poS) {
-                        f32x4 w = {oacc[qb][dt][4 * g] * invl, oacc[qb][dt][4 * g + 1] * invl,
-                                   oacc[qb][dt][4 * g + 2] * invl, oacc[qb][dt][4 * g + 3] * invl};
-                        *(f32x4*)(p.poS + prow * D + col) = w;
-                    }
-                    if (p.poL) {
-                        f32x4 w = {lacc[dt][4 * g] * invn, lacc[dt][4 * g + 1] * invn,
-                                   lacc[dt][4 * g + 2] * invn, lacc[dt][4 * g + 3] * invn};
-                        *(f32x4*)(p.poL + prow * D + col) = w;
-                    }
-                }
-        }
-    }
+    for (int qb = 0; qb < QB; ++qb)
+        finish_query_block<D, PHI>(p, qreg[qb], oacc[qb], msum[qb], m2[qb], mtrue[qb],
+                                   q_start + (wave * QB + qb) * 32 + lq, q_end, bh, t, h, lq, lin);
 }
 
 // Tile configuration: QB query blocks of 32 per wave, NW waves, BN keys per LDS
@@ -446,11 +330,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
 #ifndef REHYAT_LOCAL_STAGES
 #define REHYAT_LOCAL_STAGES 2
 #endif
-#ifndef REHYAT_LOCAL_SKEW
-#define REHYAT_LOCAL_SKEW 0
-#endif
 constexpr int kQB = REHYAT_LOCAL_QB, kNW = REHYAT_LOCAL_NW, kBN = REHYAT_LOCAL_BN, kStages = REHYAT_LOCAL_STAGES;
-constexpr bool kSkew = REHYAT_LOCAL_SKEW != 0;
 
 template <int D, int QB, int NW, int BN>
 hipError_t launch_d(const LocalParams& p, hipStream_t s) {
@@ -458,9 +338,9 @@ hipError_t launch_d(const LocalParams& p, hipStream_t s) {
     if (blocks <= 0) return hipSuccess;
     dim3 grid(blocks), block(NW * 64);
     switch (p.phi) {
-    case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone, kStages, kSkew><<<grid, block, 0, s>>>(p); break;
-    case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1, kStages, kSkew><<<grid, block, 0, s>>>(p); break;
-    case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2, kStages, kSkew><<<grid, block, 0, s>>>(p); break;
+    case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone, kStages><<<grid, block, 0, s>>>(p); break;
+    case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1, kStages><<<grid, block, 0, s>>>(p); break;
+    case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2, kStages><<<grid, block, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -1,0 +1,178 @@
+// local_common.h -- pieces shared by the bf16 local-softmax kernels: LDS tile
+// swizzle, wait-count immediates, and the epilogue that adds the linear branch
+// and applies the joint normalisation of ReHyAt (arXiv 2601.04342, §3.2 first
+// equation, with the §3.1 cached sums S_t, z_t of the §3.3 linear set).
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace rehyat {
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep a stale max while P <= 2^8
+
+// s_waitcnt immediate with expcnt and lgkmcnt at their maxima and vmcnt = 0;
+// OR in the wanted vmcnt (low 4 bits in [3:0], high 2 bits in [15:14]).
+constexpr unsigned kVmcntBase = 0x0F70;
+constexpr unsigned vm_wait_imm(int n) { return kVmcntBase | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
+
+// XOR swizzle of the 16-byte chunks of row r of an unpadded tile with C chunks
+// per row (C = head_dim / 8).  Chosen so that (a) 16 consecutive rows read at
+// one logical chunk hit 16 different 4-bank groups (K fragment reads), and (b)
+// 4 consecutive rows read at 4 consecutive logical chunks (a transposing V
+// read) land in 4 different 16-bank groups.  It depends on r mod 16 only.
+template <int C>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (C == 16) return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (C == 8) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+}
+
+// Workgroup barrier that does not drain outstanding global->LDS loads (a
+// __syncthreads() would); the compiler-only fences keep LDS accesses on their
+// side of it.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Epilogue for one block of 32 queries (lane: query lq, half h of the keys).
+// oacc holds O^T of the softmax branch scaled by 2^-m2 (log2 domain), msum the
+// lane's share of the row sum at the same scale.  When `lin`, the linear
+// branch a^L = phi(q)^T S_t, n^L = phi(q).z_t is formed with a three-pass bf16
+// split of both MFMA operands (S_t comes prepared as bf16 hi + lo parts) and
+// n^L in fp32, and the two branches are combined as
+//   y = (2^-M2' a^S + 2^-M2 a^L) / (2^-M2' n^S + 2^-M2 n^L),  M2 = max(m2, log2 n^L),
+// which equals (a^S + a^L)/(n^S + n^L) exactly and stays finite in fp32.
+// Writes y in bf16, or the per-branch partials when any partial buffer is set.
+template <int D, int PHI>
+__device__ __forceinline__ void finish_query_block(const LocalParams& p, const bf16x8 (&q)[D / 16],
+                                                   const f32x16 (&oacc)[D / 32], float msum, float m2,
+                                                   float mtrue, int row, int q_end, int bh, int t, int h,
+                                                   int lq, bool lin) {
+    constexpr int KS = D / 16, DT = D / 32;
+    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
+    constexpr int KSL = PHI == kPhiNone ? 1 : DP / 16;
+    const float lsum = xhalf_sum(msum);
+    lin = PHI != kPhiNone && lin;
+    // phi(q): n^L in fp32 and the bf16 hi/lo MFMA operands, kept in registers
+    // unless there are too many of them (then formed again per output slice)
+    constexpr bool KEEP = KSL <= 8;
+    auto phi_frag = [&](int ksl, bf16x8& fh, bf16x8& fl, float* f) {
+        float x[8];
+        unpack8(__builtin_bit_cast(u32x4, q[ksl % KS]), x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = ksl < KS ? elu1(x[j]) : x[j] * x[j];
+        u32x4 whi, wlo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float h0 = round_bf16(f[2 * j]), h1 = round_bf16(f[2 * j + 1]);
+            whi[j] = pack2_bf16(h0, h1);
+            wlo[j] = pack2_bf16(f[2 * j] - h0, f[2 * j + 1] - h1);
+        }
+        fh = __builtin_bit_cast(bf16x8, whi);
+        fl = __builtin_bit_cast(bf16x8, wlo);
+    };
+    bf16x8 fhi[KEEP ? KSL : 1], flo[KEEP ? KSL : 1];
+    float nl = 0.0f;
+    const uint16_t* shi = nullptr;
+    const uint16_t* slo = nullptr;
+    if (lin) {
+        shi = (const uint16_t*)p.s_hi + bh * p.s_bh_stride + t * p.s_chunk_stride;
+        slo = (const uint16_t*)p.s_lo + bh * p.s_bh_stride + t * p.s_chunk_stride;
+        const float* zp = p.z + bh * p.z_bh_stride + t * p.z_chunk_stride;
+        float nlp = 0.0f;
+#pragma unroll
+        for (int ksl = 0; ksl < KSL; ++ksl) {
+            float f[8];
+            bf16x8 fh, fl;
+            phi_frag(ksl, fh, fl, f);
+            if (KEEP) {
+                fhi[KEEP ? ksl : 0] = fh;
+                flo[KEEP ? ksl : 0] = fl;
+            }
+            const f32x4 z0 = *(const f32x4*)(zp + 16 * ksl + 8 * h);
+            const f32x4 z1 = *(const f32x4*)(zp + 16 * ksl + 8 * h + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) nlp += f[j] * z0[j] + f[4 + j] * z1[j];
+        }
+        nl = xhalf_sum(nlp);
+    }
+    float cs = 1.0f, cl = 0.0f;
+    if (lin && nl > 0.0f) {
+        const float M2 = fmaxf(m2, __builtin_amdgcn_logf(nl));
+        cs = __builtin_amdgcn_exp2f(m2 - M2);
+        cl = __builtin_amdgcn_exp2f(-M2);
+    }
+    const float inv = 1.0f / (cs * lsum + cl * nl);
+    const bool store_out =
+        p.pm == nullptr && p.poS == nullptr && p.poL == nullptr && p.pnt == nullptr && p.pnL == nullptr;
+    const bool valid = row < q_end;  // rows past the chunk end hold duplicated queries
+    const long long prow = bh * (long long)(p.bh_stride / D) + row;
+    if (!store_out && valid && h == 0) {
+        if (p.pm) p.pm[prow] = mtrue;
+        if (p.pnt) p.pnt[prow] = lsum * __builtin_amdgcn_exp2f(m2 - mtrue * kLog2e);
+        if (p.pnL) p.pnL[prow] = nl;
+    }
+    const float invl = 1.0f / lsum;
+    const float invn = nl > 0.0f ? 1.0f / nl : 0.0f;
+    uint16_t* ob_ptr = (uint16_t*)p.out + bh * p.bh_stride;
+    // one 32-column slice of the output at a time: a^L^T = S_t^T phi(Q)^T with a
+    // three-pass bf16 split (hi*hi + lo*hi + hi*lo) of both operands
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        f32x16 lacc = f32x16{};
+        if (lin) {
+#pragma unroll
+            for (int ksl = 0; ksl < KSL; ++ksl) {
+                const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
+                const bf16x8 ahi = __builtin_bit_cast(bf16x8, ldg_b128(shi + off));
+                const bf16x8 alo = __builtin_bit_cast(bf16x8, ldg_b128(slo + off));
+                bf16x8 fh, fl;
+                if (KEEP) {
+                    fh = fhi[KEEP ? ksl : 0];
+                    fl = flo[KEEP ? ksl : 0];
+                } else {
+                    float f[8];
+                    phi_frag(ksl, fh, fl, f);
+                }
+                lacc = mfma32x32x16(ahi, fh, lacc);
+                lacc = mfma32x32x16(alo, fh, lacc);
+                lacc = mfma32x32x16(ahi, fl, lacc);
+            }
+        }
+        if (!valid) continue;
+        if (store_out) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float y[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float num = PHI != kPhiNone ? cs * oacc[dt][4 * g + j] + cl * lacc[4 * g + j]
+                                                      : oacc[dt][4 * g + j];
+                    y[j] = num * inv;
+                }
+                u32x2 w = {pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
+                *(u32x2*)(ob_ptr + (long long)row * D + 32 * dt + 8 * g + 4 * h) = w;
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = 32 * dt + 8 * g + 4 * h;
+                if (p.poS) {
+                    f32x4 w = {oacc[dt][4 * g] * invl, oacc[dt][4 * g + 1] * invl, oacc[dt][4 * g + 2] * invl,
+                               oacc[dt][4 * g + 3] * invl};
+                    *(f32x4*)(p.poS + prow * D + col) = w;
+                }
+                if (p.poL) {
+                    f32x4 w = {lacc[4 * g] * invn, lacc[4 * g + 1] * invn, lacc[4 * g + 2] * invn,
+                               lacc[4 * g + 3] * invn};
+                    *(f32x4*)(p.poL + prow * D + col) = w;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace rehyat
