@@ -9,6 +9,7 @@
 // chunk t is the sum over u < t of the block sums (the chunk-wise RNN form).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -45,7 +46,23 @@ rehyat_status hip_fail(hipError_t e, const char* what) {
     return fail(REHYAT_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kStateSubRows = 1024;  // key rows per block-state workgroup
+constexpr int kStateSubRows = 1024;      // key rows per fp32 block-state workgroup
+constexpr int kStateSubRowsBf16 = 1600;  // key rows per bf16 block-state workgroup (25 tiles of 64)
+
+// Split of each delta block (at most `rows` keys) into sub-blocks, one
+// workgroup and one partial sum each.  The split depends on the row count
+// only, so a streaming step that folds the same rows as a forward delta block
+// adds the same partials in the same order (the two results are bitwise
+// equal).  The bf16 size gives 3 workgroups per 3-frame block of 1560-token
+// frames, 216 workgroups for 12 heads and 6 blocks.
+struct SubSplit {
+    int n_sub, sub_rows;
+};
+SubSplit state_split(int dtype, long long rows) {
+    const int sub = dtype == REHYAT_BF16 ? kStateSubRowsBf16 : kStateSubRows;
+    const long long n = (std::max<long long>(rows, 1) + sub - 1) / sub;
+    return {(int)n, sub};
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -135,12 +152,14 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct FwdWorkspace {
     size_t partial_off, shi_off, slo_off, z_off, total;
     int U, n_sub;
+    SubSplit split;
 };
 
 FwdWorkspace fwd_workspace(const Geometry& g) {
     FwdWorkspace w{};
     w.U = g.C - 1;
-    w.n_sub = (g.Tc * g.HW + kStateSubRows - 1) / kStateSubRows;
+    w.split = state_split(g.dtype, (long long)g.Tc * g.HW);
+    w.n_sub = w.split.n_sub;
     const size_t partial = (size_t)g.BH * w.U * w.n_sub * g.E * 4;
     const size_t sprep = (size_t)g.BH * g.C * g.d * g.Dp * (g.dtype == REHYAT_BF16 ? 2 : 4);
     const size_t zprep = (size_t)g.BH * g.C * g.Dp * 4;
@@ -175,7 +194,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         sp.k = k; sp.v = v; sp.kp = nullptr; sp.vp = nullptr;
         sp.bh_stride = g.N * g.d; sp.prev_bh_stride = 0; sp.prev_rows = 0;
         sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
-        sp.n_blocks = w.U; sp.sub_rows = kStateSubRows; sp.n_sub = w.n_sub; sp.stream_rows = 0;
+        sp.n_blocks = w.U; sp.sub_rows = w.split.sub_rows; sp.n_sub = w.n_sub; sp.stream_rows = 0;
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
         sp.partial = (float*)(ws + w.partial_off);
         hipError_t e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
@@ -245,7 +264,8 @@ struct StepLayout {
 StepLayout step_layout(const Geometry& g) {
     StepLayout L{};
     const size_t E = (size_t)g.E;
-    L.n_sub = (g.Tc * g.HW + kStateSubRows - 1) / kStateSubRows;
+    // sized for the largest fold (T_c frames); a step never splits into more
+    L.n_sub = state_split(g.dtype, (long long)g.Tc * g.HW).n_sub;
     size_t off = 0;
     L.S_off = off; off += align256((size_t)g.BH * E * 4);
     const size_t sprep = (size_t)g.BH * g.d * g.Dp * (g.dtype == REHYAT_BF16 ? 2 : 4);
@@ -392,8 +412,10 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
         sp.k = k; sp.v = v; sp.kp = lp.kp; sp.vp = lp.vp;
         sp.bh_stride = n * g.d; sp.prev_bh_stride = lp.prev_bh_stride; sp.prev_rows = P;
         sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
-        sp.n_blocks = 1; sp.sub_rows = kStateSubRows;
-        sp.n_sub = (evict_rows + kStateSubRows - 1) / kStateSubRows;
+        const SubSplit split = state_split(g.dtype, evict_rows);
+        if (split.n_sub > L.n_sub) return fail(REHYAT_EINVAL, "internal: state split exceeds its buffer");
+        sp.n_blocks = 1; sp.sub_rows = split.sub_rows;
+        sp.n_sub = split.n_sub;
         sp.stream_rows = evict_rows;
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
         sp.partial = (float*)(base + L.partial_off);

@@ -48,11 +48,22 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
             *(f32x4*)(p.z + off) = x;
         }
     };
-    for (int u = 0; u < p.U; ++u) {
-        emit(u);
-        for (int sp = 0; sp < p.n_sub; ++sp) {
-            const f32x4 d = *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
-            x += d;
+    // blocks of 4 delta blocks: their loads are issued together (the chain of
+    // adds is short; the latency of the loads is what costs)
+    for (int u0 = 0; u0 < p.U; u0 += 4) {
+        f32x4 d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (u0 + i < p.U)
+                for (int sp = 0; sp < p.n_sub; ++sp)
+                    d[i] += *(const f32x4*)(part + ((long long)(u0 + i) * p.n_sub + sp) * pstride);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (u0 + i >= p.U) break;
+            emit(u0 + i);
+            x += d[i];
         }
     }
     emit(p.U);

@@ -8,49 +8,103 @@
 // restricted to one block.  The cross-chunk scan adds them up into the state of
 // each chunk (the §3.3 linear set is the union of the earlier delta blocks).
 //
-// phi is applied in fp32 and split into bf16 hi + lo parts so that the bf16
-// MFMA products carry ~16 significant bits of phi(k); v is exact in bf16.
-// z is summed on the vector ALU from the unsplit fp32 phi values.
-// Both MFMA operands are read from row-major LDS tiles through the transposing
-// LDS read (key index = contraction index).
-#include "common.h"
-#include "kernels.h"
+// K and V tiles of 64 keys stream through a 4-stage LDS ring by direct
+// global->LDS loads (three tiles in flight; unpadded rows with XOR-swizzled
+// 16-byte chunks).  Eight waves (two per SIMD) share the 32-wide feature tiles
+// of D': wave w owns tiles w, w + 8, ...; when D' has fewer tiles than waves,
+// the waves sharing one split the 16-key steps and are summed at the end.
+// Both MFMA operands are read through the transposing LDS read: A = V^T (32
+// head_dim rows x 16 keys), B = phi(K) (16 keys x 32 features); phi is applied
+// to the B fragment in registers, in fp32, and split into bf16 hi + lo parts,
+// so the products carry ~16 significant bits of phi(k) while v is exact in
+// bf16.  z is summed on the vector ALU from the unsplit fp32 values.
+#include <type_traits>
+
+#include "local_common.h"
 
 namespace rehyat {
 
 namespace {
 
-template <int D, int PHI>
-__global__ __launch_bounds__(256) void state_bf16_kernel(StateParams p) {
-    constexpr int NW = 4;
-    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
-    constexpr int BN = 32;                        // keys per LDS tile
-    constexpr int VP = tr_pitch(D);               // pitches (elements) for transposing reads
-    constexpr int FP = tr_pitch(DP);
-    constexpr int VT = BN * VP, FT = BN * FP;
-    constexpr int BUF = VT + 2 * FT;              // one buffer: V, phi_hi, phi_lo
-    constexpr int DT = D / 32, NT = DP / 32;
-    constexpr int TILES = DT * NT;
-    constexpr int TPW = (TILES + NW - 1) / NW;    // output tiles per wave
-    constexpr int CHUNKS = BN * D / 8;            // 16-byte chunks per K or V tile
-    constexpr int CPT = (CHUNKS + NW * 64 - 1) / (NW * 64);
-    constexpr int E = D * DP + DP;
+#ifndef REHYAT_STATE_BN
+#define REHYAT_STATE_BN 64
+#endif
+constexpr int kStateBN = REHYAT_STATE_BN;  // keys per LDS tile
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem_raw[2 * BUF];
-    __shared__ float zred[NW * 64][8];
-    lds_u16* smem = (lds_u16*)smem_raw;
+// waves per workgroup: two per SIMD, except when D' is a single 32-wide tile
+// (then 4 waves already split the 4 16-key steps of a tile)
+constexpr int state_waves(int dp) { return dp / 32 == 1 ? 4 : 8; }
+#ifndef REHYAT_STATE_STAGES
+#define REHYAT_STATE_STAGES 4
+#endif
+constexpr int kStateStages = REHYAT_STATE_STAGES;
+
+// One wave's share of the global->LDS loads of a K/V tile (OPS instructions of
+// 1 KB: the first NINST fill the K tile, the rest the V tile).  Virtual key j <
+// prev_rows reads the overlap segment, the others read the clip at row
+// j - prev_rows.  Rows past a resource's end read as zero.
+template <int D, int BN, int NW, int OPW, int NINST>
+__device__ __forceinline__ void state_load_tile(lds_u16* base, int wave, int lane, int j0, int prev_rows,
+                                                __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                                __amdgpu_buffer_rsrc_t kprs, __amdgpu_buffer_rsrc_t vprs) {
+    constexpr int C = D / 8;
+    constexpr int rb = D * 2;
+#pragma unroll
+    for (int o = 0; o < OPW; ++o) {
+        const int op = wave + o * NW;
+        const bool isv = op >= NINST;
+        const int ins = op % NINST;
+        const int pos = 64 * ins + lane;
+        const int r = pos / C;
+        const int c16 = ((pos % C) ^ swz<C>(r)) * 16;
+        const int j = j0 + r;
+        auto* lds = (__attribute__((address_space(3))) void*)(base + (isv ? BN * D : 0) + 64 * 8 * ins);
+        if (prev_rows == 0) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, lds, 16, j * rb + c16, 0, 0, 0);
+        } else if (j >= prev_rows) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, lds, 16, (j - prev_rows) * rb + c16, 0, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vprs : kprs, lds, 16, j * rb + c16, 0, 0, 0);
+            asm volatile("");  // keeps the two loads apart (a merged load would need a per-lane resource)
+        }
+    }
+}
+
+template <int D, int PHI>
+__global__ __launch_bounds__(state_waves(PHI == kPhiPoly2 ? 2 * D : D) * 64) void state_bf16_kernel(StateParams p) {
+    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
+    constexpr int NW = state_waves(DP), BN = kStateBN, NS = kStateStages;
+    constexpr int NT = DP / 32;                       // 32-wide feature tiles
+    constexpr int NTW = NT >= NW ? NT / NW : 1;       // feature tiles per wave
+    constexpr int SPLIT = NT >= NW ? 1 : NW / NT;     // waves sharing a feature tile
+    constexpr int DT = D / 32;
+    constexpr int C = D / 8;
+    constexpr int TILE = BN * D;                      // elements of one K (or V) tile
+    constexpr int STAGE = 2 * TILE;
+    constexpr int NINST = BN * C / 64;                // 1 KB load instructions per K (or V) tile
+    constexpr int OPW = 2 * NINST / NW;               // per wave and stage
+    constexpr int KSTEPS = BN / 16;
+    static_assert(NT % NW == 0 || NW % NT == 0, "feature tiles must split evenly over the waves");
+    static_assert(2 * NINST % NW == 0, "tile loads must split evenly over the waves");
+    static_assert(KSTEPS % SPLIT == 0, "16-key steps must split evenly over the waves sharing a tile");
+    static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem_raw[NS * STAGE];
+    lds_u16* const smem = (lds_u16*)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int lq = lane & 31;
+    const int nt0 = wave % (NT >= NW ? NW : NT);      // first feature tile of the wave
+    const int kpart = wave / (NT >= NW ? NW : NT);    // which share of the 16-key steps
 
     // block -> (bh, u, sub)
-    const int blk = blockIdx.x;
+    const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
     const int per_bh = p.n_blocks * p.n_sub;
-    const int bh = blk / per_bh;
-    const int rem = blk - bh * per_bh;
+    const int bh = item / per_bh;
+    const int rem = item - bh * per_bh;
     const int u = rem / p.n_sub;
     const int sub = rem - u * p.n_sub;
 
@@ -64,170 +118,165 @@ __global__ __launch_bounds__(256) void state_bf16_kernel(StateParams p) {
     }
     const int j0 = e0 + sub * p.sub_rows;
     const int j1 = min(j0 + p.sub_rows, e1);
-    float* outp = p.partial + ((long long)(bh * p.n_blocks + u) * p.n_sub + sub) * E;
+    const int nkeys = max(j1 - j0, 0);
+    const int ntiles = (nkeys + BN - 1) / BN;
+    float* outp = p.partial + ((long long)(bh * p.n_blocks + u) * p.n_sub + sub) * (D * DP + DP);
 
+    // resources end at the block's last row: rows past it read as zero
+    const int rb = D * 2;
+    const int prev_rows = p.prev_rows;
     const uint16_t* kb = (const uint16_t*)p.k + bh * p.bh_stride;
     const uint16_t* vb = (const uint16_t*)p.v + bh * p.bh_stride;
-    const uint16_t* kpb = p.kp ? (const uint16_t*)p.kp + bh * p.prev_bh_stride : nullptr;
-    const uint16_t* vpb = p.vp ? (const uint16_t*)p.vp + bh * p.prev_bh_stride : nullptr;
-
-    f32x16 acc[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
-    float zacc[CPT][PHI == kPhiPoly2 ? 16 : 8];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-#pragma unroll
-        for (int c = 0; c < (PHI == kPhiPoly2 ? 16 : 8); ++c) zacc[i][c] = 0.0f;
-
-    const int nrows = max(j1 - j0, 0);
-    const int ntiles = (nrows + BN - 1) / BN;
-
-    u32x4 kst[CPT], vst[CPT];
-    auto load_tile = [&](int it) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NW * 64;
-            if (CHUNKS % (NW * 64) == 0 || c < CHUNKS) {
-                const int r = c / (D / 8);
-                const int col = (c % (D / 8)) * 8;
-                const int j = min(j0 + it * BN + r, j1 - 1);
-                if (j < p.prev_rows) {
-                    kst[i] = ldg_b128(kpb + (long long)j * D + col);
-                    vst[i] = ldg_b128(vpb + (long long)j * D + col);
-                } else {
-                    kst[i] = ldg_b128(kb + (long long)(j - p.prev_rows) * D + col);
-                    vst[i] = ldg_b128(vb + (long long)(j - p.prev_rows) * D + col);
-                }
-            }
-        }
+    const uint16_t* kpb = p.kp ? (const uint16_t*)p.kp + bh * p.prev_bh_stride : kb;
+    const uint16_t* vpb = p.vp ? (const uint16_t*)p.vp + bh * p.prev_bh_stride : vb;
+    const int clip_rows = max(e1 - prev_rows, 0);
+    const int prev_end = min(e1, prev_rows);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, clip_rows * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, clip_rows * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc((void*)kpb, (short)0, prev_end * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc((void*)vpb, (short)0, prev_end * rb, 0x00020000);
+    auto load_tile = [&](lds_u16* base, int t) {
+        state_load_tile<D, BN, NW, OPW, NINST>(base, wave, lane, j0 + t * BN, prev_rows, krs, vrs, kprs, vprs);
     };
-    // phi in fp32, z accumulation, hi/lo split, row-major stores into LDS
-    auto store_tile = [&](int it, int buf) {
-        lds_u16* Vd = smem + buf * BUF;
-        lds_u16* Hd = Vd + VT;
-        lds_u16* Ld = Hd + FT;
+
+    // transposing-read addressing (see lds_read_tr): for its column, lane
+    // (half h) receives keys 4h..4h+3 of the first read and 8+4h..8+4h+3 of
+    // the second; A (V^T) and B (phi(K)) use the same key order.  The swizzle
+    // depends on the row mod 16 only, so the 16-key step is an immediate.
+    const int tr_row = 4 * h + ((lane & 15) >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tr_sub = 4 * (lane & 1);
+    int toff[DT][2];  // column block c (32 columns) of a row-major K or V tile
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NW * 64;
-            if (CHUNKS % (NW * 64) == 0 || c < CHUNKS) {
-                const int r = c / (D / 8);
-                const int col = (c % (D / 8)) * 8;
-                const bool valid = j0 + it * BN + r < j1;
-                float x[8];
-                unpack8(kst[i], x);
-                float f[PHI == kPhiPoly2 ? 16 : 8];
+    for (int c = 0; c < DT; ++c) {
+        const int ch = 4 * c + tr_chunk;
+        toff[c][0] = tr_row * D + ((ch ^ swz<C>(tr_row)) << 3) + tr_sub;
+        toff[c][1] = (tr_row + 8) * D + ((ch ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
+    }
+
+    f32x16 acc[NTW][DT];
+    float zpart[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        zpart[i] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[i][dt] = f32x16{};
+    }
+
+    // the wave's 16-key steps of one tile
+    // (the tail tile masks keys past the sub-block; full tiles skip the test)
+    auto tile_steps = [&](auto tail, int t, const lds_u16* __restrict__ Ks, const lds_u16* __restrict__ Vs) {
+        constexpr bool TAIL = decltype(tail)::value;
+#pragma unroll
+        for (int s = 0; s < KSTEPS / SPLIT; ++s) {
+            const int ks = s * SPLIT + kpart;
+            const int r16 = 16 * ks * D;
+            bf16x8 a[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                a[dt] = cat(lds_read_tr(Vs, r16 + toff[dt][0]), lds_read_tr(Vs, r16 + toff[dt][1]));
+            const int kbase = t * BN + 16 * ks + 4 * h;  // key of element 0 (elements 4..7: +8)
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+                const int nt = nt0 + i * NW;
+                const int kc = (nt % (D / 32));  // K column block the features come from
+                const bool square = PHI == kPhiPoly2 && nt >= D / 32;
+                const bf16x4 k0 = lds_read_tr(Ks, r16 + toff[kc][0]);
+                const bf16x4 k1 = lds_read_tr(Ks, r16 + toff[kc][1]);
+                float f[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    f[e] = valid ? elu1(x[e]) : 0.0f;
-                    if (PHI == kPhiPoly2) f[8 + e] = valid ? x[e] * x[e] : 0.0f;
+                    const float x = (float)(e < 4 ? k0[e] : k1[e - 4]);
+                    const int key = kbase + (e < 4 ? e : e + 4);
+                    const float y = square ? x * x : elu1(x);
+                    f[e] = !TAIL || key < nkeys ? y : 0.0f;
+                    zpart[i] += f[e];
                 }
+                u32x4 whi, wlo;
 #pragma unroll
-                for (int e = 0; e < (PHI == kPhiPoly2 ? 16 : 8); ++e) zacc[i][e] += f[e];
-#pragma unroll
-                for (int half = 0; half < (PHI == kPhiPoly2 ? 2 : 1); ++half) {
-                    u32x4 whi, wlo;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float a = f[8 * half + 2 * e], b = f[8 * half + 2 * e + 1];
-                        const float ha = round_bf16(a), hb = round_bf16(b);
-                        whi[e] = pack2_bf16(ha, hb);
-                        wlo[e] = pack2_bf16(a - ha, b - hb);
-                    }
-                    lds_write_b128(Hd, r * FP + half * D + col, whi);
-                    lds_write_b128(Ld, r * FP + half * D + col, wlo);
+                for (int e = 0; e < 4; ++e) {
+                    const float h0 = round_bf16(f[2 * e]), h1 = round_bf16(f[2 * e + 1]);
+                    whi[e] = pack2_bf16(h0, h1);
+                    wlo[e] = pack2_bf16(f[2 * e] - h0, f[2 * e + 1] - h1);
                 }
-                u32x4 vv = vst[i];
-                if (!valid) vv = u32x4{0u, 0u, 0u, 0u};
-                lds_write_b128(Vd, r * VP + col, vv);
+                const bf16x8 bhi = __builtin_bit_cast(bf16x8, whi), blo = __builtin_bit_cast(bf16x8, wlo);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    acc[i][dt] = mfma32x32x16(a[dt], bhi, acc[i][dt]);
+                    acc[i][dt] = mfma32x32x16(a[dt], blo, acc[i][dt]);
+                }
             }
         }
     };
+    // the slot being filled and the slot being read never overlap; as restrict
+    // pointers they keep the transposing reads clear of a wait for the loads
+    auto iteration = [&](int t, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
+        if (t + NS - 1 < ntiles) load_tile(fill, t + NS - 1);
+        if ((t + 1) * BN <= nkeys) tile_steps(std::false_type{}, t, cur, cur + TILE);
+        else tile_steps(std::true_type{}, t, cur, cur + TILE);
+    };
 
-    const int tr_row = 8 * h + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0, 0);
-        __syncthreads();
+    for (int t = 0; t < NS - 1 && t < ntiles; ++t) load_tile(smem + t * STAGE, t);
+    for (int t = 0; t < ntiles; ++t) {
+        // own loads of tile t have landed (later tiles may be in flight), then
+        // every wave's have, and every wave is done with the slot refilled next
+        const int ahead = min(NS - 2, ntiles - 1 - t);
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
+        else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        lds_barrier();
+        iteration(t, smem + ((t + NS - 1) % NS) * STAGE, smem + (t % NS) * STAGE);
     }
-    for (int it = 0; it < ntiles; ++it) {
-        const int cur = it & 1;
-        if (it + 1 < ntiles) load_tile(it + 1);
-        const lds_u16* Vs = smem + cur * BUF;
-        const lds_u16* Hs = Vs + VT;
-        const lds_u16* Ls = Hs + FT;
+
+    // ---- write the partial: S^T in C layout (column = feature 32nt + lq, row
+    // d = 32dt + (r/4)*8 + 4h + r%4), z from the two lane halves; waves that
+    // share a feature tile are summed through LDS first
+    float z[NTW];
 #pragma unroll
-        for (int ks = 0; ks < BN / 16; ++ks) {
-            const int row = 16 * ks + tr_row;
+    for (int i = 0; i < NTW; ++i) z[i] = xhalf_sum(zpart[i]);
+    if (SPLIT > 1) {
+        __syncthreads();  // the ring is reused
+        float* red = (float*)smem_raw;  // [SPLIT-1][NT][DT][16][64] + z [SPLIT-1][NT][32]
+        float* zred = red + (SPLIT - 1) * NT * DT * 16 * 64;
+        if (kpart > 0) {
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int tix = wave + i * NW;
-                if (TILES % NW == 0 || tix < TILES) {
-                    const int dt = tix / NT, nt = tix % NT;
-                    const int vcol = 32 * dt + tr_col, fcol = 32 * nt + tr_col;
-                    const bf16x8 a = cat(lds_read_tr(Vs, row * VP + vcol), lds_read_tr(Vs, (row + 4) * VP + vcol));
-                    const bf16x8 bh_ = cat(lds_read_tr(Hs, row * FP + fcol), lds_read_tr(Hs, (row + 4) * FP + fcol));
-                    const bf16x8 bl_ = cat(lds_read_tr(Ls, row * FP + fcol), lds_read_tr(Ls, (row + 4) * FP + fcol));
-                    acc[i] = mfma32x32x16(a, bh_, acc[i]);
-                    acc[i] = mfma32x32x16(a, bl_, acc[i]);
-                }
-            }
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[((((kpart - 1) * NT + nt0) * DT + dt) * 16 + r) * 64 + lane] = acc[0][dt][r];
+            if (lane < 32) zred[((kpart - 1) * NT + nt0) * 32 + lq] = z[0];
         }
-        if (it + 1 < ntiles) store_tile(it + 1, cur ^ 1);
         __syncthreads();
-    }
-
-    // S^T partial: C layout, lane column = feature 32nt + lq, rows d = 32dt + (r/4)*8 + 4h + r%4
+        if (kpart > 0) return;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int tix = wave + i * NW;
-        if (TILES % NW == 0 || tix < TILES) {
-            const int dt = tix / NT, nt = tix % NT;
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int sp = 1; sp < SPLIT; ++sp) acc[0][dt][r] += red[((((sp - 1) * NT + nt0) * DT + dt) * 16 + r) * 64 + lane];
+#pragma unroll
+        for (int sp = 1; sp < SPLIT; ++sp) z[0] += lane < 32 ? zred[((sp - 1) * NT + nt0) * 32 + lq] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int f = 32 * (nt0 + i * NW) + lq;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int drow = 32 * dt + (r >> 2) * 8 + 4 * h + (r & 3);
-                outp[(long long)drow * DP + 32 * nt + lq] = acc[i][r];
+                outp[(long long)drow * DP + f] = acc[i][dt][r];
             }
-        }
-    }
-    // z partial: threads with the same column chunk (tid % (D/8)) hold sums over
-    // different rows; reduce them through LDS
-    constexpr int COLS = D / 8;
-    constexpr int ZW = PHI == kPhiPoly2 ? 16 : 8;
-#pragma unroll
-    for (int half = 0; half < ZW / 8; ++half) {
-        float part[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            part[e] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) part[e] += zacc[i][8 * half + e];
-            zred[tid][e] = part[e];
-        }
-        __syncthreads();
-        if (tid < COLS) {
-            float s[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] = 0.0f;
-            for (int r = tid; r < NW * 64; r += COLS)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s[e] += zred[r][e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) outp[D * DP + half * D + 8 * tid + e] = s[e];
-        }
-        __syncthreads();
+        if (lane < 32) outp[(long long)D * DP + f] = z[i];
     }
 }
 
 template <int D>
 hipError_t launch_d(const StateParams& p, hipStream_t s) {
-    const int blocks = p.BH * p.n_blocks * p.n_sub;
+    const long long blocks = (long long)p.BH * p.n_blocks * p.n_sub;
     if (blocks <= 0) return hipSuccess;
     switch (p.phi) {
-    case kPhiElu1: state_bf16_kernel<D, kPhiElu1><<<blocks, 256, 0, s>>>(p); break;
-    case kPhiPoly2: state_bf16_kernel<D, kPhiPoly2><<<blocks, 256, 0, s>>>(p); break;
+    case kPhiElu1: state_bf16_kernel<D, kPhiElu1><<<(unsigned)blocks, state_waves(D) * 64, 0, s>>>(p); break;
+    case kPhiPoly2: state_bf16_kernel<D, kPhiPoly2><<<(unsigned)blocks, state_waves(2 * D) * 64, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
