@@ -11,7 +11,9 @@ Prints ONE JSON line: tokens/s of the whole step, the local-softmax kernel
 against the bf16 MFMA roofline (its duration taken from HIP events recorded
 around that kernel on its own stream during the timed steps), the state pass
 against the HBM roofline, the dense bidirectional softmax companion at the same
-shape, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+shape, the bidirectional hybrid form (§3.2 with overlap: later chunks join the
+linear set) at the same shape, and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -36,7 +38,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
 LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "6c41cdbd02b2b01f", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (249464 * 2.0 + 98478 * 1.0) * 1024}
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (249477 * 2.0 + 98599 * 1.0) * 1024}
 
 
 LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h")
@@ -107,14 +109,18 @@ def geometry_counts(w, Tc, To, phi_dim):
     lin_rows = max((C - 1) * Tc - To, 0) * HW if phi_dim > 0 else 0
     E = d * phi_dim + phi_dim
     state_bytes = 2.0 * BH * lin_rows * d * 2 + 3.0 * (C - 1) * BH * E * 4 if phi_dim > 0 else 0.0
+    # bidirectional form (§3.2 with overlap): every key of the clip lies in a
+    # block; 2C+1 block sums written and read, C prepared states written
+    bidir_bytes = (2.0 * BH * F * HW * d * 2 + 2.0 * (2 * C + 1) * BH * E * 4 + C * BH * E * 4
+                   if phi_dim > 0 and C >= 2 else 0.0)
     return {"softmax_flops": flops, "exps": float(pairs * BH), "state_bytes": state_bytes,
-            "chunks": C}
+            "bidir_state_bytes": bidir_bytes, "chunks": C}
 
 
-def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=True):
+def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=True, causal=True):
     import torch
     for _ in range(warmup):
-        rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out)
+        rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out, causal=causal)
     torch.cuda.synchronize()
     evs = [[hip.event() for _ in range(4)] for _ in range(steps)] if profile else None
     if torch.distributed.is_available() and torch.distributed.is_initialized():
@@ -124,7 +130,7 @@ def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=Tru
     for i in range(steps):
         if profile:
             rh.set_profile_events(evs[i])
-        rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out)
+        rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out, causal=causal)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if profile:
@@ -179,6 +185,7 @@ def main():
     ap.add_argument("--chunk-frames", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-bidir", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -244,6 +251,21 @@ def main():
                  "hybrid_speedup": round(d_t["ms_per_step"] / main_t["ms_per_step"], 3),
                  "flop_ratio": round(dc["softmax_flops"] / cnt["softmax_flops"], 3)}
 
+    bidir = None
+    if not args.no_bidir:
+        b_t = time_steps(rh, hip, qg, kg, vg, out, w, Tc, To, phi, max(3, args.steps // 2), 1, causal=False)
+        bidir = {"tokens_per_s": round(w.tokens / (b_t["ms_per_step"] / 1000.0), 1),
+                 "ms_per_step": round(b_t["ms_per_step"], 4),
+                 "local_ms": round(b_t["local_ms"], 4),
+                 "local_tflops": round(cnt["softmax_flops"] / (b_t["local_ms"] / 1000.0) / 1e12, 2)}
+        if phi_dim > 0:
+            bst = b_t["state_ms"] + b_t["scan_ms"]
+            bidir.update(state_kernel_ms=round(b_t["state_ms"], 4), scan_ms=round(b_t["scan_ms"], 4),
+                         state_pass_gbs=round(cnt["bidir_state_bytes"] / (bst / 1000.0) / 1e9, 1),
+                         state_pass_frac=round(cnt["bidir_state_bytes"] / (bst / 1000.0) / 1e9
+                                               / PEAK_HBM_GBS, 4),
+                         state_algorithmic_bytes=cnt["bidir_state_bytes"])
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, Tc, To, phi, args.cpu_seconds)
@@ -261,6 +283,7 @@ def main():
         "roofline": roofline,
         "state_pass": state,
         "dense_softmax": dense,
+        "bidirectional": bidir,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -99,6 +99,31 @@ rehyat_status rehyat_attn_fwd_partials(const void* q, const void* k, const void*
                                        int feature_map, void* stream);
 
 /*
+ * Bidirectional (non-causal) form, ReHyAt §3.2 with overlap (second partition
+ * equation): the softmax set of chunk t is the same window as above, and the
+ * linear set is every other key of the clip -- the keys before the window and
+ * the keys of every later chunk.  Same arguments, layouts, ownership, errors
+ * and stream behaviour as rehyat_attn_fwd / rehyat_attn_fwd_f32.  The linear
+ * state of chunk t is formed as a prefix plus a suffix of block sums (two
+ * separate fp32 sums, never a total minus the window).  There is no streaming
+ * form: a chunk's output depends on later chunks.
+ */
+rehyat_status rehyat_attn_fwd_bidir(const void* q, const void* k, const void* v, void* out,
+                                    int B, int H, int frames, int tokens_per_frame, int head_dim,
+                                    int chunk_frames, int overlap_frames, int feature_map,
+                                    void* stream);
+rehyat_status rehyat_attn_fwd_bidir_f32(const void* q, const void* k, const void* v, void* out,
+                                        int B, int H, int frames, int tokens_per_frame, int head_dim,
+                                        int chunk_frames, int overlap_frames, int feature_map,
+                                        void* stream);
+/* Per-query partials of the bidirectional form (see rehyat_attn_fwd_partials). */
+rehyat_status rehyat_attn_fwd_bidir_partials(const void* q, const void* k, const void* v, int dtype,
+                                             float* m, float* nt, float* o_s, float* o_l, float* n_l,
+                                             int B, int H, int frames, int tokens_per_frame,
+                                             int head_dim, int chunk_frames, int overlap_frames,
+                                             int feature_map, void* stream);
+
+/*
  * Streaming (chunk-wise RNN) form, §3.3: one call per chunk of frames, with
  * memory that does not depend on how many frames have been processed.
  *

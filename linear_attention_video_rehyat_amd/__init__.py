@@ -28,6 +28,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 # every entry point declared in include/rehyat.h
 exported_symbols = (
     "rehyat_attn_fwd", "rehyat_attn_fwd_f32", "rehyat_attn_fwd_partials",
+    "rehyat_attn_fwd_bidir", "rehyat_attn_fwd_bidir_f32", "rehyat_attn_fwd_bidir_partials",
     "rehyat_step_state_bytes", "rehyat_step_state_init", "rehyat_attn_step",
     "rehyat_set_profile_events", "rehyat_status_string", "rehyat_last_error", "rehyat_version",
 )
@@ -65,11 +66,12 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, f_p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float)
     sig_fwd = [vp, vp, vp, vp] + [i] * 8 + [vp]
-    for name in ("rehyat_attn_fwd", "rehyat_attn_fwd_f32"):
+    for name in ("rehyat_attn_fwd", "rehyat_attn_fwd_f32", "rehyat_attn_fwd_bidir", "rehyat_attn_fwd_bidir_f32"):
         fn = getattr(lib, name)
         fn.argtypes, fn.restype = sig_fwd, i
-    lib.rehyat_attn_fwd_partials.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp] + [i] * 8 + [vp]
-    lib.rehyat_attn_fwd_partials.restype = i
+    for name in ("rehyat_attn_fwd_partials", "rehyat_attn_fwd_bidir_partials"):
+        fn = getattr(lib, name)
+        fn.argtypes, fn.restype = [vp, vp, vp, i, vp, vp, vp, vp, vp] + [i] * 8 + [vp], i
     lib.rehyat_step_state_bytes.argtypes = [i] * 8
     lib.rehyat_step_state_bytes.restype = ctypes.c_size_t
     lib.rehyat_step_state_init.argtypes = [ctypes.POINTER(_StepStateC), vp, ctypes.c_size_t] + [i] * 8
@@ -135,9 +137,11 @@ def _check_qkv(q, k, v):
 
 
 def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, feature_map="elu1",
-             out=None, stream=None):
+             out=None, stream=None, causal=True):
     """Whole-clip hybrid attention forward.  q, k, v: [B, H, frames*tokens_per_frame, d]
-    (bf16 or fp32, contiguous, on the GPU).  Returns ``out`` (allocated if None)."""
+    (bf16 or fp32, contiguous, on the GPU).  Returns ``out`` (allocated if None).
+    causal=False selects the bidirectional form (keys of later chunks join the
+    linear set)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -148,7 +152,11 @@ def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, fe
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise RehyatError(1, "out must match q")
-    fn = lib.rehyat_attn_fwd if _dtype_id(q) == DTYPE_BF16 else lib.rehyat_attn_fwd_f32
+    bf16 = _dtype_id(q) == DTYPE_BF16
+    if causal:
+        fn = lib.rehyat_attn_fwd if bf16 else lib.rehyat_attn_fwd_f32
+    else:
+        fn = lib.rehyat_attn_fwd_bidir if bf16 else lib.rehyat_attn_fwd_bidir_f32
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, frames,
               tokens_per_frame, d, chunk_frames, overlap_frames, feature_map_id(feature_map),
               _stream_handle(stream)))
@@ -156,7 +164,7 @@ def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, fe
 
 
 def attn_fwd_partials(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames,
-                      feature_map="elu1", stream=None):
+                      feature_map="elu1", stream=None, causal=True):
     """Per-query partials of both branches (verification aid): dict with m, nt,
     o_s, o_l, n_l as fp32 tensors (see include/rehyat.h)."""
     torch = _torch()
@@ -167,7 +175,8 @@ def attn_fwd_partials(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_f
     parts = {"m": torch.empty(B, H, N, **f32), "nt": torch.empty(B, H, N, **f32),
              "o_s": torch.empty(B, H, N, d, **f32), "o_l": torch.empty(B, H, N, d, **f32),
              "n_l": torch.empty(B, H, N, **f32)}
-    _check(lib.rehyat_attn_fwd_partials(
+    fn = lib.rehyat_attn_fwd_partials if causal else lib.rehyat_attn_fwd_bidir_partials
+    _check(fn(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_id(q),
         parts["m"].data_ptr(), parts["nt"].data_ptr(), parts["o_s"].data_ptr(),
         parts["o_l"].data_ptr(), parts["n_l"].data_ptr(), B, H, frames, tokens_per_frame, d,

@@ -150,15 +150,19 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of the whole-clip forward: partial block sums and prepared states.
 struct FwdWorkspace {
-    size_t partial_off, shi_off, slo_off, z_off, total;
+    size_t partial_off, shi_off, slo_off, z_off, suffix_off, total;
     int U, n_sub;
     SubSplit split;
 };
 
-FwdWorkspace fwd_workspace(const Geometry& g) {
+FwdWorkspace fwd_workspace(const Geometry& g, int mode) {
     FwdWorkspace w{};
-    w.U = g.C - 1;
-    w.split = state_split(g.dtype, (long long)g.Tc * g.HW);
+    w.U = state_block_count(mode, g.C);
+    // longest block: T_c frames (recurrent form); max(r, T_c - r) frames with
+    // r = T_o mod T_c, or T_c when r = 0 (bidirectional form)
+    long long block_frames = g.Tc;
+    if (mode == kBidirectional && g.To % g.Tc != 0) block_frames = std::max(g.To % g.Tc, g.Tc - g.To % g.Tc);
+    w.split = state_split(g.dtype, block_frames * g.HW);
     w.n_sub = w.split.n_sub;
     const size_t partial = (size_t)g.BH * w.U * w.n_sub * g.E * 4;
     const size_t sprep = (size_t)g.BH * g.C * g.d * g.Dp * (g.dtype == REHYAT_BF16 ? 2 : 4);
@@ -167,24 +171,30 @@ FwdWorkspace fwd_workspace(const Geometry& g) {
     w.shi_off = align256(partial);
     w.slo_off = w.shi_off + align256(sprep);
     w.z_off = w.slo_off + (g.dtype == REHYAT_BF16 ? align256(sprep) : 0);
-    w.total = w.z_off + align256(zprep);
+    w.suffix_off = w.z_off + align256(zprep);
+    const size_t suffix = mode == kBidirectional ? (size_t)g.BH * g.C * g.E * 4 : 0;
+    w.total = w.suffix_off + align256(suffix);
     return w;
 }
 
-// A chunk t has a linear set iff t T_c - T_o > 0; the last chunk is t = C-1.
-bool any_linear(const Geometry& g) {
-    return g.phi != REHYAT_PHI_NONE && (long long)(g.C - 1) * g.Tc - g.To > 0;
+// Recurrent form: chunk t has a linear set iff t T_c - T_o > 0 (the last chunk
+// is t = C-1).  Bidirectional form: every chunk's window misses some key as
+// soon as there are two chunks.
+bool any_linear(const Geometry& g, int mode) {
+    if (g.phi == REHYAT_PHI_NONE) return false;
+    if (mode == kBidirectional) return g.C >= 2;
+    return (long long)(g.C - 1) * g.Tc - g.To > 0;
 }
 
-rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g,
+rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g, int mode,
                       float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s) {
-    const bool lin = any_linear(g);
+    const bool lin = any_linear(g, mode);
     char* ws = nullptr;
     FwdWorkspace w{};
     hipError_t pe = prof_mark(0, s);
     if (pe != hipSuccess) return hip_fail(pe, "hipEventRecord");
     if (lin) {
-        w = fwd_workspace(g);
+        w = fwd_workspace(g, mode);
         void* p = nullptr;
         rehyat_status st = arena_get(w.total, &p);
         if (st != REHYAT_OK) return st;
@@ -196,6 +206,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
         sp.n_blocks = w.U; sp.sub_rows = w.split.sub_rows; sp.n_sub = w.n_sub; sp.stream_rows = 0;
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
+        sp.mode = mode; sp.F = g.F;
         sp.partial = (float*)(ws + w.partial_off);
         hipError_t e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
@@ -207,7 +218,9 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         cp.s_chunk_stride = (long long)g.d * g.Dp; cp.s_bh_stride = (long long)g.C * g.d * g.Dp;
         cp.z_chunk_stride = g.Dp; cp.z_bh_stride = (long long)g.C * g.Dp;
         cp.U = w.U; cp.n_sub = w.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
-        cp.t_first = 1; cp.t_offset = 0; cp.f32_prep = g.dtype == REHYAT_F32;
+        cp.t_first = mode == kBidirectional ? 0 : 1; cp.t_offset = 0; cp.f32_prep = g.dtype == REHYAT_F32;
+        cp.mode = mode; cp.C = g.C; cp.q = g.To / g.Tc;
+        cp.suffix = mode == kBidirectional ? (float*)(ws + w.suffix_off) : nullptr;
         e = launch_scan(cp, s);
         if (e != hipSuccess) return hip_fail(e, "scan launch");
     } else {
@@ -224,7 +237,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
     lp.tiles_per_chunk = (int)((rows_per_chunk + bm - 1) / bm);
     const long long blocks = (long long)g.BH * g.C * lp.tiles_per_chunk;
     if (blocks > 0x7fffffffLL) return fail(REHYAT_EINVAL, "problem too large: %lld workgroups", blocks);
-    lp.phi = g.phi; lp.lin_always = 0;
+    lp.phi = g.phi; lp.lin_always = mode == kBidirectional ? 1 : 0;
     if (lin) {
         lp.s_hi = ws + w.shi_off; lp.s_lo = ws + w.slo_off; lp.z = (const float*)(ws + w.z_off);
         lp.s_chunk_stride = (long long)g.d * g.Dp; lp.s_bh_stride = (long long)g.C * g.d * g.Dp;
@@ -240,7 +253,8 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
 }
 
 rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, int B, int H,
-                        int frames, int tpf, int d, int Tc, int To, int phi, int dtype, void* stream) {
+                        int frames, int tpf, int d, int Tc, int To, int phi, int dtype, int mode,
+                        void* stream) {
     Geometry g{};
     rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
     if (st != REHYAT_OK) return st;
@@ -251,7 +265,22 @@ rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, 
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
         return fail(REHYAT_EINVAL, "out must not overlap q, k or v");
     g_last_error.clear();
-    return run_fwd(q, k, v, out, g, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream);
+    return run_fwd(q, k, v, out, g, mode, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream);
+}
+
+rehyat_status partials_entry(const void* q, const void* k, const void* v, int dtype, float* m, float* nt,
+                             float* o_s, float* o_l, float* n_l, int B, int H, int frames, int tpf, int d,
+                             int Tc, int To, int phi, int mode, void* stream) {
+    Geometry g{};
+    rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
+    if (st != REHYAT_OK) return st;
+    if (!q || !k || !v) return fail(REHYAT_EINVAL, "null tensor pointer");
+    if (!m && !nt && !o_s && !o_l && !n_l) return fail(REHYAT_EINVAL, "no partial output requested");
+    const void* ptrs[8] = {q, k, v, m, nt, o_s, o_l, n_l};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(REHYAT_EINVAL, "pointers must be 16-byte aligned");
+    g_last_error.clear();
+    return run_fwd(q, k, v, nullptr, g, mode, m, nt, o_s, o_l, n_l, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- streaming state
@@ -290,7 +319,7 @@ rehyat_status rehyat_attn_fwd(const void* q, const void* k, const void* v, void*
                               int frames, int tokens_per_frame, int head_dim, int chunk_frames,
                               int overlap_frames, int feature_map, void* stream) {
     return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
-                     overlap_frames, feature_map, REHYAT_BF16, stream);
+                     overlap_frames, feature_map, REHYAT_BF16, kCausal, stream);
 }
 
 rehyat_status rehyat_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, int B,
@@ -298,7 +327,22 @@ rehyat_status rehyat_attn_fwd_f32(const void* q, const void* k, const void* v, v
                                   int chunk_frames, int overlap_frames, int feature_map,
                                   void* stream) {
     return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
-                     overlap_frames, feature_map, REHYAT_F32, stream);
+                     overlap_frames, feature_map, REHYAT_F32, kCausal, stream);
+}
+
+rehyat_status rehyat_attn_fwd_bidir(const void* q, const void* k, const void* v, void* out, int B, int H,
+                                    int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+                                    int overlap_frames, int feature_map, void* stream) {
+    return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
+                     overlap_frames, feature_map, REHYAT_BF16, kBidirectional, stream);
+}
+
+rehyat_status rehyat_attn_fwd_bidir_f32(const void* q, const void* k, const void* v, void* out, int B,
+                                        int H, int frames, int tokens_per_frame, int head_dim,
+                                        int chunk_frames, int overlap_frames, int feature_map,
+                                        void* stream) {
+    return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
+                     overlap_frames, feature_map, REHYAT_F32, kBidirectional, stream);
 }
 
 rehyat_status rehyat_attn_fwd_partials(const void* q, const void* k, const void* v, int dtype,
@@ -306,17 +350,17 @@ rehyat_status rehyat_attn_fwd_partials(const void* q, const void* k, const void*
                                        int B, int H, int frames, int tokens_per_frame,
                                        int head_dim, int chunk_frames, int overlap_frames,
                                        int feature_map, void* stream) {
-    Geometry g{};
-    rehyat_status st = check_common(g, B, H, frames, tokens_per_frame, head_dim, chunk_frames,
-                                    overlap_frames, feature_map, dtype);
-    if (st != REHYAT_OK) return st;
-    if (!q || !k || !v) return fail(REHYAT_EINVAL, "null tensor pointer");
-    if (!m && !nt && !o_s && !o_l && !n_l) return fail(REHYAT_EINVAL, "no partial output requested");
-    const void* ptrs[8] = {q, k, v, m, nt, o_s, o_l, n_l};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return fail(REHYAT_EINVAL, "pointers must be 16-byte aligned");
-    g_last_error.clear();
-    return run_fwd(q, k, v, nullptr, g, m, nt, o_s, o_l, n_l, (hipStream_t)stream);
+    return partials_entry(q, k, v, dtype, m, nt, o_s, o_l, n_l, B, H, frames, tokens_per_frame, head_dim,
+                          chunk_frames, overlap_frames, feature_map, kCausal, stream);
+}
+
+rehyat_status rehyat_attn_fwd_bidir_partials(const void* q, const void* k, const void* v, int dtype,
+                                             float* m, float* nt, float* o_s, float* o_l, float* n_l,
+                                             int B, int H, int frames, int tokens_per_frame,
+                                             int head_dim, int chunk_frames, int overlap_frames,
+                                             int feature_map, void* stream) {
+    return partials_entry(q, k, v, dtype, m, nt, o_s, o_l, n_l, B, H, frames, tokens_per_frame, head_dim,
+                          chunk_frames, overlap_frames, feature_map, kBidirectional, stream);
 }
 
 size_t rehyat_step_state_bytes(int B, int H, int tokens_per_frame, int head_dim, int chunk_frames,
@@ -418,6 +462,7 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
         sp.n_sub = split.n_sub;
         sp.stream_rows = evict_rows;
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
+        sp.mode = kCausal; sp.F = frames;
         sp.partial = (float*)(base + L.partial_off);
         e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
@@ -430,6 +475,7 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
         cp.z_chunk_stride = 0; cp.z_bh_stride = g.Dp;
         cp.U = 1; cp.n_sub = sp.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
         cp.t_first = 1; cp.t_offset = 1; cp.f32_prep = g.dtype == REHYAT_F32;
+        cp.mode = kCausal; cp.C = 1; cp.q = 0; cp.suffix = nullptr;
         e = launch_scan(cp, s);
         if (e != hipSuccess) return hip_fail(e, "scan launch");
         nonempty = true;

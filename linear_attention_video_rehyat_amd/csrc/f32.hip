@@ -162,8 +162,10 @@ __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
         e0 = 0;
         e1 = p.stream_rows;
     } else {
-        e0 = max(u * p.Tc - p.To, 0) * p.HW;
-        e1 = max((u + 1) * p.Tc - p.To, 0) * p.HW;
+        int fa, fb;
+        state_block_frames(p.mode, u, p.Tc, p.To, p.F, fa, fb);
+        e0 = fa * p.HW;
+        e1 = fb * p.HW;
     }
     const int j0 = e0 + sub * p.sub_rows;
     const int j1 = min(j0 + p.sub_rows, e1);

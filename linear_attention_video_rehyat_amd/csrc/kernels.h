@@ -11,6 +11,41 @@ enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiPoly2 = 2 };
 
 inline int feature_dim(int phi, int d) { return phi == kPhiElu1 ? d : (phi == kPhiPoly2 ? 2 * d : 0); }
 
+// Partition of the keys into the blocks whose linear sums the state pass forms
+// (frame ranges, times tokens_per_frame for rows).
+//  kCausal: the delta blocks E_u = frames [max(u T_c - T_o, 0), max((u+1) T_c - T_o, 0)),
+//   u = 0 .. C-2: the keys that leave the softmax window between chunk u and
+//   u+1, so the linear set of chunk t (ReHyAt §3.3) is E_0 + ... + E_{t-1}.
+//  kBidirectional: the frames cut at every c T_c - r and c T_c (r = T_o mod
+//   T_c), clipped to [0, F): block 2c = [c T_c - r, c T_c), block 2c+1 =
+//   [c T_c, (c+1) T_c - r), c = 0 .. C (2C+1 blocks).  The softmax window of
+//   chunk t (§3.2, with overlap) starts at the start of block 2(t - q), q =
+//   T_o div T_c (clipped at block 0), and ends at the start of block 2t+3, so
+//   its linear set (every key outside the window) is the blocks before
+//   max(2(t - q), 0) plus the blocks from 2t+3 on.
+enum BlockMode { kCausal = 0, kBidirectional = 1 };
+
+__host__ __device__ inline int state_block_count(int mode, int C) { return mode == kCausal ? C - 1 : 2 * C + 1; }
+
+__host__ __device__ inline void state_block_frames(int mode, int u, int Tc, int To, int F, int& f0, int& f1) {
+    if (mode == kCausal) {
+        f0 = u * Tc - To > 0 ? u * Tc - To : 0;
+        f1 = (u + 1) * Tc - To > 0 ? (u + 1) * Tc - To : 0;
+        return;
+    }
+    const int r = To % Tc, c = u >> 1;
+    int a, b;
+    if ((u & 1) == 0) {
+        a = c * Tc - r;
+        b = c * Tc;
+    } else {
+        a = c * Tc;
+        b = (c + 1) * Tc - r;
+    }
+    f0 = a < 0 ? 0 : (a > F ? F : a);
+    f1 = b < 0 ? 0 : (b > F ? F : b);
+}
+
 // Local-softmax + fused hybrid combine (one launch covers every (b, h, chunk,
 // query tile)).  Key rows of a window are addressed through a virtual index j:
 // j < prev_rows reads the "prev" segment (the streaming overlap frames), the
@@ -54,6 +89,7 @@ struct StateParams {
     int n_sub;                        // sub-blocks per delta block (max over blocks)
     int stream_rows;                  // streaming: rows of [prev | chunk] to fold (U = 1); 0 in fwd
     int BH, d, phi;
+    int mode, F;                      // block partition (BlockMode) and frames of the clip
     float* partial;                   // [BH][U][n_sub][d*D' + D']
 };
 
@@ -70,6 +106,10 @@ struct ScanParams {
     int t_first;                      // first prepared state to write
     int t_offset;                     // prepared state X_t is written at slot t - t_offset
     int f32_prep;                     // prepared form is fp32 (s_hi) rather than bf16 hi/lo
+    // kBidirectional: U = 2C+1 blocks; chunk t gets the sum of the blocks
+    // before max(2(t - q), 0) plus the blocks from 2t+3 on (q = T_o div T_c)
+    int mode, C, q;
+    float* suffix;                    // [BH][C][E] fp32 scratch for the suffix sums
 };
 
 // Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot.

@@ -6,7 +6,10 @@
 // softmax window before it.  This kernel forms that exclusive prefix in fp32,
 // sequentially in u (one thread per 4 state elements), and writes each X_t in
 // the form the local kernel's epilogue consumes: S^T split into bf16 hi + lo
-// parts (or fp32 for the fp32 path) and z in fp32.
+// parts (or fp32 for the fp32 path) and z in fp32.  For the bidirectional form
+// (§3.2 with overlap: the linear set is every key outside the window, later
+// chunks included) the state of chunk t is a prefix plus a suffix of the block
+// sums, kept as two separate sums rather than a total minus the window.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,6 +51,35 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
             *(f32x4*)(p.z + off) = x;
         }
     };
+    auto block_sum = [&](int u) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < p.n_sub; ++sp) d += *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
+        return d;
+    };
+    if (p.mode == kBidirectional) {
+        // suffix sums Y_k = sum of blocks k.. U-1, backwards; chunk t needs
+        // Y_{2t+3} (zero past the last block).  Each thread keeps its own 4
+        // elements, so the scratch needs no synchronisation.
+        float* suf = p.suffix + (long long)bh * p.C * E + e4;
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < p.C; ++t)
+            if (2 * t + 3 >= p.U) *(f32x4*)(suf + (long long)t * E) = y;
+        for (int k = p.U - 1; k >= 0; --k) {
+            y += block_sum(k);
+            if (k >= 3 && (k & 1) && (k - 3) / 2 < p.C) *(f32x4*)(suf + (long long)((k - 3) / 2) * E) = y;
+        }
+        // prefix sums, forwards; chunk t adds the blocks before max(2(t-q), 0)
+        int k = 0;
+        for (int t = 0; t < p.C; ++t) {
+            const int pk = max(2 * (t - p.q), 0);
+            for (; k < pk; ++k) x += block_sum(k);
+            const f32x4 keep = x;
+            x += *(const f32x4*)(suf + (long long)t * E);
+            emit(t);
+            x = keep;
+        }
+        return;
+    }
     // blocks of 4 delta blocks: their loads are issued together (the chain of
     // adds is short; the latency of the loads is what costs)
     for (int u0 = 0; u0 < p.U; u0 += 4) {

@@ -1,7 +1,8 @@
 // state_bf16.hip -- phi-map + block-state kernel (bf16 inputs, fp32 state).
 //
-// For each delta block E_u of keys (the keys that leave the softmax window
-// between chunk u and chunk u+1) and each contiguous sub-block of it, computes
+// For each block of keys of the state partition (the delta blocks E_u of the
+// recurrent form, or the finer blocks of the bidirectional form; see
+// state_block_frames) and each contiguous sub-block of it, computes
 //   S^T_partial = sum_j v_j phi(k_j)^T   ([head_dim][D'], fp32)
 //   z_partial   = sum_j phi(k_j)         ([D'], fp32)
 // -- the cached linear-attention sums of ReHyAt §3.1 (arXiv 2601.04342),
@@ -113,8 +114,10 @@ __global__ __launch_bounds__(state_waves(PHI == kPhiPoly2 ? 2 * D : D) * 64) voi
         e0 = 0;
         e1 = p.stream_rows;
     } else {
-        e0 = max(u * p.Tc - p.To, 0) * p.HW;
-        e1 = max((u + 1) * p.Tc - p.To, 0) * p.HW;
+        int fa, fb;
+        state_block_frames(p.mode, u, p.Tc, p.To, p.F, fa, fb);
+        e0 = fa * p.HW;
+        e1 = fb * p.HW;
     }
     const int j0 = e0 + sub * p.sub_rows;
     const int j1 = min(j0 + p.sub_rows, e1);

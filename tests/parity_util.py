@@ -58,9 +58,9 @@ def check_f32(y, ref, what=""):
     return r
 
 
-def oracle_rows(q, k, v, frames, HW, Tc, To, phi, rows=None, partials=False):
+def oracle_rows(q, k, v, frames, HW, Tc, To, phi, rows=None, partials=False, causal=True):
     return O.definition(to64(q), to64(k), to64(v), frames, HW, Tc, To, phi, rows=rows,
-                        partials=partials)
+                        partials=partials, causal=causal)
 
 
 def gpu(*ts):
