@@ -289,10 +289,24 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     // being read are passed as restrict pointers: they never overlap, and the
     // compiler may then keep the transposing V reads clear of the wait for the
     // loads still in flight (it cannot otherwise tell them apart).
+    // the linear branch's prepared state S_t^T (elu+1: [D][D], hi and lo parts)
+    // is staged in LDS by the last iteration, into the slot no tile needs any
+    // more, so the epilogue reads it from there instead of every wave loading
+    // it from L2
+    const bool lin = PHI != kPhiNone && (p.lin_always || w0 > 0);
+    constexpr bool STAGE_S = PHI == kPhiElu1 && 2 * D * D <= STAGE;
+    const uint16_t* shi = nullptr;
+    const uint16_t* slo = nullptr;
+    if (STAGE_S && lin) {
+        shi = (const uint16_t*)p.s_hi + bh * p.s_bh_stride + t * p.s_chunk_stride;
+        slo = (const uint16_t*)p.s_lo + bh * p.s_bh_stride + t * p.s_chunk_stride;
+    }
     auto iteration = [&](int it, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
         if (it + PF < ntiles)
             issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(fill, wave, it + PF, p.prev_rows, seg_shift, rb, op_row,
                                                            op_c16, krs, vrs, kprs, vprs);
+        else if (STAGE_S && lin && it == ntiles - 1)
+            issue_state_dma<D, D, NW>(fill, wave, lane, shi, slo);
         scores_softmax(it, cur);
         pv(cur + KTILE);
     };
@@ -309,11 +323,16 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     }
 
     // ---------------------------------------------------------------- epilogue
-    const bool lin = PHI != kPhiNone && (p.lin_always || w0 > 0);
+    const lds_u16* s_lds = nullptr;
+    if (STAGE_S && lin) {
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // own share of the staged state
+        lds_barrier();                               // everyone's
+        s_lds = smem + ((ntiles - 1 + PF) % STAGES) * STAGE;
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
         finish_query_block<D, PHI>(p, qreg[qb], oacc[qb], msum[qb], m2[qb], mtrue[qb],
-                                   q_start + (wave * QB + qb) * 32 + lq, q_end, bh, t, h, lq, lin);
+                                   q_start + (wave * QB + qb) * 32 + lq, q_end, bh, t, h, lq, lin, s_lds);
 }
 
 // Tile configuration: QB query blocks of 32 per wave, NW waves, BN keys per LDS

@@ -46,11 +46,37 @@ __device__ __forceinline__ void lds_barrier() {
 //   y = (2^-M2' a^S + 2^-M2 a^L) / (2^-M2' n^S + 2^-M2 n^L),  M2 = max(m2, log2 n^L),
 // which equals (a^S + a^L)/(n^S + n^L) exactly and stays finite in fp32.
 // Writes y in bf16, or the per-branch partials when any partial buffer is set.
+// Global->LDS copy of the prepared state S_t^T (bf16 hi part at dst, lo part
+// right after it, each [D][DP] row-major with the 16-byte chunks of row r
+// XOR-swizzled by swz(r)), spread over the NW waves of a workgroup.
+template <int D, int DP, int NW>
+__device__ __forceinline__ void issue_state_dma(lds_u16* dst, int wave, int lane, const uint16_t* shi,
+                                                const uint16_t* slo) {
+    constexpr int CS = DP / 8;                   // 16-byte chunks per row
+    constexpr int NI = D * DP * 2 / 1024;        // 1 KB instructions per matrix
+    constexpr int PER = (NI + NW - 1) / NW;
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc((void*)shi, (short)0, D * DP * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)slo, (short)0, D * DP * 2, 0x00020000);
+#pragma unroll
+    for (int o = 0; o < PER; ++o) {
+        const int ins = wave + o * NW;
+        if (NI % NW == 0 || ins < NI) {
+            const int pos = 64 * ins + lane;
+            const int r = pos / CS;
+            const int off = r * DP * 2 + ((pos % CS) ^ swz<CS>(r)) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, (__attribute__((address_space(3))) void*)(dst + 512 * ins),
+                                                     16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                lrs, (__attribute__((address_space(3))) void*)(dst + D * DP + 512 * ins), 16, off, 0, 0, 0);
+        }
+    }
+}
+
 template <int D, int PHI>
 __device__ __forceinline__ void finish_query_block(const LocalParams& p, const bf16x8 (&q)[D / 16],
                                                    const f32x16 (&oacc)[D / 32], float msum, float m2,
                                                    float mtrue, int row, int q_end, int bh, int t, int h,
-                                                   int lq, bool lin) {
+                                                   int lq, bool lin, const lds_u16* s_lds = nullptr) {
     constexpr int KS = D / 16, DT = D / 32;
     constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
     constexpr int KSL = PHI == kPhiNone ? 1 : DP / 16;
@@ -126,9 +152,16 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
         if (lin) {
 #pragma unroll
             for (int ksl = 0; ksl < KSL; ++ksl) {
-                const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
-                const bf16x8 ahi = __builtin_bit_cast(bf16x8, ldg_b128(shi + off));
-                const bf16x8 alo = __builtin_bit_cast(bf16x8, ldg_b128(slo + off));
+                bf16x8 ahi, alo;
+                if (s_lds) {  // copy staged in LDS by issue_state_dma (DP / 8 chunks per row)
+                    const int off = (32 * dt + lq) * DP + (((2 * ksl + h) ^ swz<DP / 8>(lq)) << 3);
+                    ahi = lds_read_b128(s_lds, off);
+                    alo = lds_read_b128(s_lds, D * DP + off);
+                } else {
+                    const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
+                    ahi = __builtin_bit_cast(bf16x8, ldg_b128(shi + off));
+                    alo = __builtin_bit_cast(bf16x8, ldg_b128(slo + off));
+                }
                 bf16x8 fh, fl;
                 if (KEEP) {
                     fh = fhi[KEEP ? ksl : 0];
