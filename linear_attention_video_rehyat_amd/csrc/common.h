@@ -88,12 +88,18 @@ __device__ __forceinline__ u32x4 ldg_b128(const uint16_t* p) {
     return *(const u32x4*)p;
 }
 
-// Swap values between the two 32-lane halves of a wave and combine.
+// Combine the values of lanes l and l ^ 32 (the two halves of a wave).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; with both operands x, the two results hold, in
+// every lane l, x[l % 32] and x[32 + l % 32] (no LDS traffic, unlike a
+// shuffle through ds_bpermute).
 __device__ __forceinline__ float xhalf_max(float x) {
-    return fmaxf(x, __shfl_xor(x, 32));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
-    return x + __shfl_xor(x, 32);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Map a linear block index so that consecutive logical work items land on the
