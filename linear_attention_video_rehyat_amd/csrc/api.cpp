@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -107,6 +108,65 @@ rehyat_status check_common(Geometry& g, int B, int H, int frames, int tpf, int d
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
+}
+
+// ---------------------------------------------------------------- local-kernel dispatch order
+// The local kernel's workgroups differ in cost (chunk 0 streams a shorter
+// window).  Simulate the dispatcher -- each XCD hands its workgroups, in order,
+// to whichever of its CUs frees up first -- for the natural and the
+// longest-first order of each XCD's items (local_work_item), and keep the
+// longest-first order where it finishes earlier.  Decisions are cached per
+// geometry.
+long long local_makespan(const LocalParams& lp, int blocks, int bn, int cus_per_xcd) {
+    long long worst = 0;
+    std::vector<long long> cu(cus_per_xcd);
+    for (int x = 0; x < 8; ++x) {
+        std::fill(cu.begin(), cu.end(), 0);
+        for (int bid = x; bid < blocks; bid += 8) {
+            const int item = local_work_item(lp, bid, blocks, bn);
+            const int t = (item / lp.tiles_per_chunk) % lp.n_chunks;
+            auto it = std::min_element(cu.begin(), cu.end());
+            *it += chunk_key_tiles(lp, t, bn) + 2;  // + the epilogue, about two key tiles
+        }
+        worst = std::max(worst, *std::max_element(cu.begin(), cu.end()));
+    }
+    return worst;
+}
+
+int cus_per_xcd() {
+    static std::mutex mu;
+    static std::vector<int> per_dev;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 32;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1, 0);
+    if (per_dev[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+        per_dev[dev] = n / 8;
+    }
+    return per_dev[dev];
+}
+
+int choose_lpt_order(const LocalParams& lp, int blocks, int bn) {
+    if (lp.n_chunks < 2 || blocks < 16) return 0;
+    const int cpx = cus_per_xcd();
+    static std::mutex mu;
+    static std::map<std::vector<long long>, int> cache;
+    const std::vector<long long> key = {lp.BH, lp.n_chunks, lp.tiles_per_chunk, lp.F, lp.Tc, lp.To, lp.HW,
+                                        lp.prev_rows, bn, cpx, blocks};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto f = cache.find(key);
+        if (f != cache.end()) return f->second;
+    }
+    LocalParams a = lp, b = lp;
+    a.lpt_order = 0;
+    b.lpt_order = 1;
+    const int use = local_makespan(b, blocks, bn, cpx) < local_makespan(a, blocks, bn, cpx) ? 1 : 0;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = use;
+    return use;
 }
 
 // ---------------------------------------------------------------- workspace arena
@@ -238,6 +298,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
     const long long blocks = (long long)g.BH * g.C * lp.tiles_per_chunk;
     if (blocks > 0x7fffffffLL) return fail(REHYAT_EINVAL, "problem too large: %lld workgroups", blocks);
     lp.phi = g.phi; lp.lin_always = mode == kBidirectional ? 1 : 0;
+    lp.lpt_order = g.dtype == REHYAT_BF16 ? choose_lpt_order(lp, (int)blocks, local_bf16_key_tile(g.d)) : 0;
     if (lin) {
         lp.s_hi = ws + w.shi_off; lp.s_lo = ws + w.slo_off; lp.z = (const float*)(ws + w.z_off);
         lp.s_chunk_stride = (long long)g.d * g.Dp; lp.s_bh_stride = (long long)g.C * g.d * g.Dp;

@@ -74,7 +74,52 @@ struct LocalParams {
     long long z_chunk_stride, z_bh_stride;
     // optional partials (verification aid): fp32
     float* pm; float* pnt; float* poS; float* poL; float* pnL;
+    int lpt_order;            // dispatch each XCD's work items longest first (see local_work_item)
 };
+
+// Key tiles of BN keys that a query tile of chunk t streams (its softmax window).
+__host__ __device__ inline int chunk_key_tiles(const LocalParams& p, int t, int BN) {
+    const int f0 = t * p.Tc;
+    const int f1 = f0 + p.Tc < p.F ? f0 + p.Tc : p.F;
+    const int w0 = f0 - p.To > 0 ? f0 - p.To : 0;
+    const int nkeys = p.prev_rows + (f1 - w0) * p.HW;
+    return (nkeys + BN - 1) / BN;
+}
+
+// Work item of workgroup `bid` of the local kernel.  The dispatcher deals
+// workgroups round-robin over the 8 XCDs, so workgroup bid is the (bid / 8)-th
+// one XCD bid % 8 receives, and each XCD hands its workgroups to its CUs as
+// they free up.  Each XCD owns a contiguous share of the items (item = (bh *
+// n_chunks + t) * tiles_per_chunk + query tile), so the query tiles of a chunk
+// share that XCD's L2.  With lpt_order the share is taken in order of
+// decreasing cost (key tiles of the chunk), chunk by chunk, so the greedy
+// assignment ends on the short items; otherwise in natural order.
+__host__ __device__ inline int local_work_item(const LocalParams& p, int bid, int nblocks, int BN) {
+    const int per = nblocks / 8, tail = nblocks % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    const int s = xcd < tail ? xcd * (per + 1) : tail * (per + 1) + (xcd - tail) * per;
+    if (!p.lpt_order) return s + idx;
+    const int e = s + per + (xcd < tail ? 1 : 0);
+    const int T = p.tiles_per_chunk;
+    const int gs = s / T, ge = (e - 1) / T;  // chunk groups meeting [s, e)
+    int rem = idx, level = 1 << 30;
+    for (;;) {
+        int c = -1;  // the largest cost below `level`
+        for (int g = gs; g <= ge; ++g) {
+            const int cg = chunk_key_tiles(p, g % p.n_chunks, BN);
+            if (cg < level && cg > c) c = cg;
+        }
+        if (c < 0) return s + idx;  // unreachable: every position lies in some group
+        for (int g = gs; g <= ge; ++g) {
+            if (chunk_key_tiles(p, g % p.n_chunks, BN) != c) continue;
+            const int a = g * T > s ? g * T : s;
+            const int b = (g + 1) * T < e ? (g + 1) * T : e;
+            if (rem < b - a) return a + rem;
+            rem -= b - a;
+        }
+        level = c;
+    }
+}
 
 // Block-state pass: partial S^T = sum phi(k) v^T (stored [d][D'] fp32) and
 // z = sum phi(k) over contiguous key sub-blocks of each delta block E_u.
@@ -128,6 +173,7 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s);
 
 int local_bf16_tile_rows(int d);   // queries per workgroup of the bf16 local kernel
+int local_bf16_key_tile(int d);    // keys per LDS tile of the bf16 local kernel
 int local_f32_tile_rows(int d);
 
 }  // namespace rehyat

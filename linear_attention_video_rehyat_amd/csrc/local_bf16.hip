@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
 
     // block -> (bh, chunk, query tile); integer division is expanded on the
     // vector ALU, so pin the (uniform) results to scalar registers
-    const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    const int item = __builtin_amdgcn_readfirstlane(local_work_item(p, blockIdx.x, gridDim.x, BN));
     const int per_bh = p.n_chunks * p.tiles_per_chunk;
     const int bh = __builtin_amdgcn_readfirstlane(item / per_bh);
     const int rem = item - bh * per_bh;
@@ -369,6 +369,7 @@ hipError_t launch_d(const LocalParams& p, hipStream_t s) {
 }  // namespace
 
 int local_bf16_tile_rows(int) { return kQB * kNW * 32; }
+int local_bf16_key_tile(int) { return kBN; }
 
 hipError_t launch_local_bf16(const LocalParams& p, hipStream_t s) {
     switch (p.d) {
