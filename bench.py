@@ -37,11 +37,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "6c41cdbd02b2b01f", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (249477 * 2.0 + 98599 * 1.0) * 1024}
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "2c23fbfabad2682a", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (257694 * 2.0 + 101477 * 1.0) * 1024}
 
 
-LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h")
+LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h", "kernels.h")
 
 
 def local_kernel_sha():

@@ -124,3 +124,23 @@ def test_binding_fails_loudly_without_gpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(rh.RehyatError):
         rh.attn_fwd(q, q, q, 1, 8, 1, 0)
+
+
+def test_local_work_order_is_a_permutation(tmp_path):
+    """The local kernel's workgroup -> work-item map (natural and longest-first
+    order) is a bijection that keeps each XCD's share of items; host-side build
+    of kernels.h with hipcc, run on the CPU."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    src = os.path.join(ROOT, "tests", "native", "work_order_check.cpp")
+    exe = str(tmp_path / "work_order_check")
+    csrc = os.path.join(ROOT, "linear_attention_video_rehyat_amd", "csrc")
+    build = subprocess.run([hipcc, "-O1", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", f"-I{csrc}",
+                            src, "-o", exe], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "0 violations" in run.stdout
