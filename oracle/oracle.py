@@ -32,7 +32,7 @@ import subprocess
 
 import numpy as np
 
-PHI_NONE, PHI_ELU1, PHI_POLY2 = 0, 1, 2
+PHI_NONE, PHI_ELU1, PHI_POLY2, PHI_GIVEN = 0, 1, 2, 3
 PHI_NAMES = {"none": PHI_NONE, "elu1": PHI_ELU1, "poly2": PHI_POLY2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,9 +42,68 @@ _lib = None
 
 
 def phi_kind(phi) -> int:
+    """Kind of a feature-map argument: a name or code of a fixed map, or a pair
+    (phi_q, phi_k) of callables (separate maps for queries and keys, such as two
+    :class:`MlpFeatureMap` objects), which is PHI_GIVEN."""
+    if isinstance(phi, (tuple, list)):
+        return PHI_GIVEN
     if isinstance(phi, str):
         return PHI_NAMES[phi.lower()]
     return int(phi)
+
+
+class MlpFeatureMap:
+    """Learned polynomial feature map of ReHyAt.
+
+    §3.2 (the equation after the partitions) writes phi as the concatenation of
+    powers psi_p(x)^p, p = 1..P; §4.3 (model hyperparameters) and appendix §7.1
+    make psi a two-layer MLP with degree 2, separate maps for keys and queries,
+    about 2.4M parameters per converted block.  Readings where the pages are
+    silent: the MLP is Linear -> ReLU -> Linear per head, with biases; its
+    output of 2m values is split into psi_1 (first m) and psi_2 (last m); the
+    degree-1 part is made non-negative (§3.1 requires phi >= 0) as 1 + elu, so
+
+        hidden = relu(W1[h] x + b1[h]),  psi = W2[h] hidden + b2[h],
+        phi(x) = [1 + elu(psi_1), psi_2 * psi_2]            (D' = 2m)
+
+    W1: [H, hidden, d], b1: [H, hidden], W2: [H, 2m, hidden], b2: [H, 2m].
+    With H = 12, d = 128, hidden = 256 and m = 128, the query and key maps of
+    one block hold 12 * 2 * (256*128 + 256 + 256*256 + 256) = 2.37M parameters.
+    """
+
+    def __init__(self, w1, b1, w2, b2):
+        self.w1, self.b1, self.w2, self.b2 = (_f64(a) for a in (w1, b1, w2, b2))
+        H, hid, _ = self.w1.shape
+        assert self.b1.shape == (H, hid)
+        assert self.w2.shape[0] == H and self.w2.shape[2] == hid and self.w2.shape[1] % 2 == 0
+        assert self.b2.shape == self.w2.shape[:2]
+
+    @property
+    def dim(self) -> int:
+        return self.w2.shape[1]
+
+    def __call__(self, x) -> np.ndarray:
+        x = _f64(x)                                   # [B, H, N, d]
+        assert x.shape[1] == self.w1.shape[0] and x.shape[-1] == self.w1.shape[2]
+        hid = np.maximum(np.einsum("bhnd,hkd->bhnk", x, self.w1) + self.b1[None, :, None, :], 0.0)
+        psi = np.einsum("bhnk,hmk->bhnm", hid, self.w2) + self.b2[None, :, None, :]
+        m = psi.shape[-1] // 2
+        p1, p2 = psi[..., :m], psi[..., m:]
+        return np.concatenate([np.where(p1 > 0, p1 + 1.0, np.exp(np.minimum(p1, 0.0))), p2 * p2], axis=-1)
+
+
+def feature_q(x, phi):
+    """phi of query rows for any feature-map argument (see :func:`phi_kind`)."""
+    return phi[0](x) if phi_kind(phi) == PHI_GIVEN else feature_map(x, phi)
+
+
+def feature_k(x, phi):
+    """phi of key rows for any feature-map argument (see :func:`phi_kind`)."""
+    return phi[1](x) if phi_kind(phi) == PHI_GIVEN else feature_map(x, phi)
+
+
+def features(q, k, phi):
+    return feature_q(q, phi), feature_k(k, phi)
 
 
 def build(force: bool = False) -> str:
@@ -68,7 +127,8 @@ def _load():
         lp = ctypes.POINTER(ctypes.c_longlong)
         lib.rehyat_oracle_fwd.restype = ctypes.c_int
         lib.rehyat_oracle_fwd.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 8 + [
-            ctypes.c_double, ctypes.c_int, lp, ctypes.c_longlong, dp, dp, dp, dp, dp, ctypes.c_int]
+            ctypes.c_double, ctypes.c_int, lp, ctypes.c_longlong, dp, dp, dp, dp, dp, ctypes.c_int,
+            dp, dp, ctypes.c_int]
         lib.rehyat_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -103,6 +163,10 @@ def definition(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, 
     assert k.shape == q.shape and v.shape == q.shape
     assert N == frames * tokens_per_frame
     kind = phi_kind(phi)
+    fq = fk = None
+    if kind == PHI_GIVEN:
+        fq, fk = (np.ascontiguousarray(a) for a in features(q, k, phi))
+        assert fq.shape == fk.shape and fq.shape[:3] == (B, H, N)
     if rows is not None:
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         R = rows.shape[0]
@@ -122,7 +186,8 @@ def definition(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, 
         rows_p, R,
         _ptr(parts["m"]) if parts else None, _ptr(parts["nt"]) if parts else None,
         _ptr(parts["oS"]) if parts else None, _ptr(parts["oL"]) if parts else None,
-        _ptr(parts["nL"]) if parts else None, int(nthreads))
+        _ptr(parts["nL"]) if parts else None, int(nthreads),
+        _ptr(fq), _ptr(fk), fq.shape[-1] if fq is not None else 0)
     if st == 1:
         raise ValueError("oracle: invalid arguments")
     if st == 2:
@@ -175,7 +240,8 @@ def brute_force(q, k, v, tokens_per_frame, chunk_frames, overlap_frames, phi="el
     s = scale * (q @ np.swapaxes(k, -1, -2))
     w = np.where(m_s, np.exp(np.where(m_s, s, 0.0)), 0.0)
     if phi_kind(phi) != PHI_NONE:
-        w = w + np.where(m_l, feature_map(q, phi) @ np.swapaxes(feature_map(k, phi), -1, -2), 0.0)
+        fq, fk = features(q, k, phi)
+        w = w + np.where(m_l, fq @ np.swapaxes(fk, -1, -2), 0.0)
     return (w @ v) / w.sum(axis=-1, keepdims=True)
 
 
@@ -193,8 +259,8 @@ class RecurrentState:
                  phi="elu1", scale=1.0):
         self.HW, self.d = tokens_per_frame, head_dim
         self.Tc, self.To = chunk_frames, overlap_frames
-        self.phi, self.scale = phi_kind(phi), scale
-        Dp = feature_map(np.zeros((1, head_dim)), phi).shape[-1]
+        self.phi, self.scale = (phi if phi_kind(phi) == PHI_GIVEN else phi_kind(phi)), scale
+        Dp = feature_k(np.zeros((B, H, 1, head_dim)), self.phi).shape[-1]
         self.S = np.zeros((B, H, Dp, head_dim))
         self.z = np.zeros((B, H, Dp))
         self.k_prev = np.zeros((B, H, 0, head_dim))
@@ -218,7 +284,7 @@ class RecurrentState:
         e = np.exp(self.scale * (qc @ np.swapaxes(kw, -1, -2)))     # softmax set
         a_s = e @ vw
         n_s = e.sum(axis=-1)
-        fq = feature_map(qc, self.phi)                               # linear set
+        fq = feature_q(qc, self.phi)                                 # linear set
         a_l = fq @ self.S
         n_l = (fq * self.z[:, :, None, :]).sum(axis=-1)
         y = (a_s + a_l) / (n_s + n_l)[..., None]                     # joint normalisation
@@ -228,7 +294,7 @@ class RecurrentState:
         keep = min(self.To, self.frames_done) * self.HW
         n_ev = kw.shape[-2] - keep
         if n_ev > 0:
-            fk = feature_map(kw[:, :, :n_ev], self.phi)
+            fk = feature_k(kw[:, :, :n_ev], self.phi)
             self.S = self.S + np.swapaxes(fk, -1, -2) @ vw[:, :, :n_ev]
             self.z = self.z + fk.sum(axis=-2)
         self.k_prev = kw[:, :, n_ev:]

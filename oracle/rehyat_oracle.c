@@ -29,7 +29,9 @@
  *   - the overlap is the T_o frames *preceding* a chunk, clipped at frame 0;
  *   - same phi for queries and keys; ELU1 = elu(x)+1 (alpha = 1), POLY2 =
  *     [elu(x)+1 ; x*x] (a parameter-free degree-2 instance of the polynomial
- *     feature map of §3.2), NONE = no linear branch.
+ *     feature map of §3.2), NONE = no linear branch; GIVEN = caller-supplied
+ *     phi(q) and phi(k) rows (the learned maps, separate for queries and keys,
+ *     of §4.3 and appendix §7.1).
  *
  * The exponential is the literal one, with no max subtraction: every key weight
  * is exactly exp(s).  That is finite in fp64 while s < 709; the function reports
@@ -46,7 +48,9 @@
 #include <string.h>
 #include <omp.h>
 
-enum { ORACLE_PHI_NONE = 0, ORACLE_PHI_ELU1 = 1, ORACLE_PHI_POLY2 = 2 };
+/* GIVEN: the caller passes phi(q) and phi(k) for every row (a learned map,
+ * evaluated by the caller from its definition; the same sums follow). */
+enum { ORACLE_PHI_NONE = 0, ORACLE_PHI_ELU1 = 1, ORACLE_PHI_POLY2 = 2, ORACLE_PHI_GIVEN = 3 };
 
 /* elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise (§3.1). */
 static double elu1(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
@@ -88,6 +92,8 @@ static void feature_map(int phi_kind, const double* x, int d, double* out) {
  *   causal  : 1 = recurrent partition of §3.3 (keys after the chunk ignored);
  *             0 = non-causal partition of §3.2 (they join the linear set).
  *   nthreads: OpenMP threads (<= 0: library default).
+ *   fq, fk  : with phi_kind GIVEN, phi(q) and phi(k) of every row, [B][H][N][Dg]
+ *             fp64 (Dg = D' >= 1); ignored otherwise.
  *
  * Returns 0 on success, 1 on invalid arguments, 2 if a sum is not finite.
  */
@@ -95,10 +101,12 @@ int rehyat_oracle_fwd(const double* q, const double* k, const double* v, double*
                       int B, int H, int F, int HW, int d, int Tc, int To, int phi_kind,
                       double scale, int causal, const long long* rows, long long nrows,
                       double* part_m, double* part_nt, double* part_oS, double* part_oL,
-                      double* part_nL, int nthreads) {
+                      double* part_nL, int nthreads, const double* fq, const double* fk, int Dg) {
     if (!q || !k || !v || !y || B < 1 || H < 1 || F < 1 || HW < 1 || d < 1 || Tc < 1 || To < 0)
         return 1;
-    const int Dp = rehyat_oracle_feature_dim(phi_kind, d);
+    const int given = phi_kind == ORACLE_PHI_GIVEN;
+    if (given && (!fq || !fk || Dg < 1)) return 1;
+    const int Dp = given ? Dg : rehyat_oracle_feature_dim(phi_kind, d);
     if (Dp < 0) return 1;
     const long long N = (long long)F * HW;
     const long long R = rows ? nrows : N;
@@ -111,7 +119,7 @@ int rehyat_oracle_fwd(const double* q, const double* k, const double* v, double*
 
     /* phi applied once to every key row. */
     double* phik = NULL;
-    if (Dp > 0) {
+    if (Dp > 0 && !given) {
         phik = (double*)malloc(sizeof(double) * (size_t)B * H * N * Dp);
         if (!phik) return 1;
 #pragma omp parallel for schedule(static)
@@ -132,7 +140,7 @@ int rehyat_oracle_fwd(const double* q, const double* k, const double* v, double*
             const double* qi = q + (bh * N + i) * d;
             const double* kb = k + bh * N * d;
             const double* vb = v + bh * N * d;
-            const double* pk = phik ? phik + bh * N * Dp : NULL;
+            const double* pk = given ? fk + bh * N * Dp : (phik ? phik + bh * N * Dp : NULL);
 
             /* chunk of query i and its softmax window, in token units */
             const long long f = i / HW;
@@ -143,7 +151,8 @@ int rehyat_oracle_fwd(const double* q, const double* k, const double* v, double*
             if (w1f > F) w1f = F;
             const long long w0 = w0f * HW, w1 = w1f * HW;
 
-            if (Dp > 0) feature_map(phi_kind, qi, d, phiq);
+            if (given) memcpy(phiq, fq + (bh * N + i) * Dp, sizeof(double) * Dp);
+            else if (Dp > 0) feature_map(phi_kind, qi, d, phiq);
             for (int c = 0; c < d; ++c) { aS[c] = 0.0; aL[c] = 0.0; }
             double nS = 0.0, nL = 0.0, m = -INFINITY;
 

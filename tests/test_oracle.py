@@ -281,3 +281,92 @@ def test_bad_arguments():
         O.definition(q, q, q, 2, 2, 0, 0, "elu1")
     with pytest.raises(ValueError):
         O.definition(q, q, q, 2, 2, 1, -1, "elu1")
+
+
+# ------------------------------------------------ learned (MLP) feature maps
+
+def _reduction_weights(H, d, shift1=0.0, shift2=0.0, gain2=1.0):
+    """MLP weights whose map has a closed form: W1 = [I; -I] (hidden = 2d, so
+    relu splits x into its positive and negative parts), W2 = [[I, -I]; [g I, -g I]]
+    (psi_1 = x + shift1, psi_2 = g x + shift2)."""
+    I = np.eye(d)
+    w1 = np.tile(np.concatenate([I, -I])[None], (H, 1, 1))
+    b1 = np.zeros((H, 2 * d))
+    w2 = np.tile(np.block([[I, -I], [gain2 * I, -gain2 * I]])[None], (H, 1, 1))
+    b2 = np.tile(np.concatenate([np.full(d, shift1), np.full(d, shift2)])[None], (H, 1))
+    return O.MlpFeatureMap(w1, b1, w2, b2)
+
+
+def _closed(shift1=0.0, shift2=0.0, gain2=1.0):
+    def phi(x):
+        a = x + shift1
+        b = gain2 * x + shift2
+        return np.concatenate([np.where(a > 0, a + 1.0, np.exp(np.minimum(a, 0.0))), b * b], axis=-1)
+    return phi
+
+
+def test_mlp_map_reduces_to_poly2():
+    """With W1 = [I; -I], W2 = [[I, -I]; [I, -I]] and zero biases, relu(x) - relu(-x)
+    = x makes psi_1 = psi_2 = x, so the learned map is exactly [1 + elu(x), x^2]
+    (the parameter-free degree-2 map) and every attention form agrees with it."""
+    rng = np.random.default_rng(11)
+    B, H, F, HW, d = 1, 2, 5, 3, 4
+    q, k, v = rand_qkv(rng, B, H, F * HW, d)
+    m = _reduction_weights(H, d)
+    np.testing.assert_array_equal(m(q), O.feature_map(q, "poly2"))
+    for causal in (True, False):
+        ref = O.definition(q, k, v, F, HW, 2, 1, "poly2", causal=causal)
+        assert rel(O.definition(q, k, v, F, HW, 2, 1, (m, m), causal=causal), ref) <= 1e-14
+        assert rel(O.brute_force(q, k, v, HW, 2, 1, (m, m), causal=causal), ref) <= 1e-12
+    assert rel(O.recurrent(q, k, v, F, HW, 2, 1, (m, m)), O.definition(q, k, v, F, HW, 2, 1, "poly2")) <= 1e-12
+
+
+def test_mlp_zero_second_half_is_elu1():
+    """psi_2 = 0 (zero lower half of W2 and b2) leaves [1 + elu(x), 0]: the zero
+    features add nothing, so the hybrid equals the ELU1 one."""
+    rng = np.random.default_rng(12)
+    q, k, v = rand_qkv(rng, 2, 1, 12, 3)
+    m = _reduction_weights(1, 3, gain2=0.0)
+    for causal in (True, False):
+        ref = O.definition(q, k, v, 4, 3, 1, 2, "elu1", causal=causal)
+        assert rel(O.definition(q, k, v, 4, 3, 1, 2, (m, m), causal=causal), ref) <= 1e-14
+
+
+def test_mlp_separate_query_and_key_maps():
+    """Queries go through phi_q and keys through phi_k (§7.1: separate maps).  With
+    shifted biases and a gain the two maps differ and have closed forms; swapping
+    them changes the result."""
+    rng = np.random.default_rng(13)
+    B, H, F, HW, d = 1, 2, 6, 2, 3
+    q, k, v = rand_qkv(rng, B, H, F * HW, d)
+    mq = _reduction_weights(H, d, shift1=0.3, shift2=-0.5)
+    mk = _reduction_weights(H, d, shift1=-0.7, shift2=0.25, gain2=2.0)
+    cq, ck = _closed(0.3, -0.5), _closed(-0.7, 0.25, 2.0)
+    np.testing.assert_allclose(mq(q), cq(q), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(mk(k), ck(k), rtol=1e-14, atol=1e-14)
+    for causal in (True, False):
+        want = O.brute_force(q, k, v, HW, 1, 1, (cq, ck), causal=causal)
+        got = O.definition(q, k, v, F, HW, 1, 1, (mq, mk), causal=causal)
+        assert rel(got, want) <= 1e-12
+        swapped = O.definition(q, k, v, F, HW, 1, 1, (mk, mq), causal=causal)
+        assert rel(swapped, want) > 1e-3
+    assert rel(O.recurrent(q, k, v, F, HW, 1, 1, (mq, mk)), O.brute_force(q, k, v, HW, 1, 1, (cq, ck))) <= 1e-12
+
+
+def test_mlp_map_random_weights_small_loops():
+    """Random weights on a tiny case: the map against the two layers written as
+    scalar loops over units (catches an index or transpose slip in the tensor form),
+    and phi >= 0."""
+    rng = np.random.default_rng(14)
+    H, d, hid, m2 = 2, 3, 5, 4
+    w1, b1 = rng.standard_normal((H, hid, d)), rng.standard_normal((H, hid))
+    w2, b2 = rng.standard_normal((H, m2, hid)), rng.standard_normal((H, m2))
+    x = rng.standard_normal((1, H, 4, d))
+    got = O.MlpFeatureMap(w1, b1, w2, b2)(x)
+    for h in range(H):
+        for n in range(4):
+            hidden = [max(sum(w1[h, a, c] * x[0, h, n, c] for c in range(d)) + b1[h, a], 0.0) for a in range(hid)]
+            psi = [sum(w2[h, o, a] * hidden[a] for a in range(hid)) + b2[h, o] for o in range(m2)]
+            want = [p + 1.0 if p > 0 else math.exp(p) for p in psi[:m2 // 2]] + [p * p for p in psi[m2 // 2:]]
+            np.testing.assert_allclose(got[0, h, n], want, rtol=1e-13)
+    assert (got >= 0).all()
