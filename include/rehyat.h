@@ -46,8 +46,10 @@ extern "C" {
 typedef enum rehyat_feature_map {
     REHYAT_PHI_NONE = 0,  /* no linear branch: softmax over the local window only */
     REHYAT_PHI_ELU1 = 1,  /* phi(x) = elu(x) + 1 (alpha 1), D' = head_dim (§3.1) */
-    REHYAT_PHI_POLY2 = 2  /* phi(x) = [elu(x) + 1, x*x], D' = 2 head_dim: a parameter-free
+    REHYAT_PHI_POLY2 = 2, /* phi(x) = [elu(x) + 1, x*x], D' = 2 head_dim: a parameter-free
                              degree-2 instance of the polynomial map of §3.2 */
+    REHYAT_PHI_MLP2 = 3   /* learned degree-2 map (see rehyat_mlp_weights), D' = 2 head_dim;
+                             only through the _mlp entry points, which take its weights */
 } rehyat_feature_map;
 
 typedef enum rehyat_status {
@@ -164,6 +166,60 @@ rehyat_status rehyat_step_state_init(rehyat_step_state* st, void* buf, size_t by
  */
 rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void* k, const void* v,
                                void* out, int frames, void* stream);
+
+/*
+ * Learned feature maps (ReHyAt §3.2, the polynomial map phi(x) = [psi_1(x),
+ * psi_2(x)^2] after the partition equations; §4.3 "Model Hyperparameters" and
+ * appendix §7.1: psi is a two-layer MLP of degree 2, with separate maps for
+ * queries and keys).  Per head h and row x (head_dim values):
+ *
+ *   hidden = relu(W1[h] x + b1[h])               (`hidden` values)
+ *   psi    = W2[h] hidden + b2[h]                (2 head_dim values)
+ *   phi(x) = [1 + elu(psi[0:d]), psi[d:2d]^2]    (D' = 2 head_dim, phi >= 0)
+ *
+ * The MLP's shape is a reading of the pages (Linear-ReLU-Linear with biases;
+ * the degree-1 part made non-negative as 1 + elu, as §3.1 requires of phi).
+ * bf16 calls: W1, W2 in bf16, products accumulated in fp32, the hidden layer
+ * and phi rounded to bf16 (a bf16 model's activation precision); the linear
+ * state is still accumulated in fp32.  fp32 calls: everything in fp32.
+ * All pointers are device pointers, 16-byte aligned, owned by the caller.
+ */
+typedef struct rehyat_mlp_weights {
+    const void* w1;   /* [H][hidden][head_dim], dtype of the call */
+    const float* b1;  /* [H][hidden] fp32 */
+    const void* w2;   /* [H][2 head_dim][hidden], dtype of the call */
+    const float* b2;  /* [H][2 head_dim] fp32 */
+    int hidden;       /* 32, 64, 128 or 256 (the same for the query and key maps) */
+} rehyat_mlp_weights;
+
+/* phi of every row: x [B][H][rows][head_dim] -> phi [B][H][rows][2 head_dim], both
+ * in dtype (REHYAT_BF16 or REHYAT_F32); phi must not overlap x.  The map the
+ * forward entry points below apply to q (with phi_q) and k (with phi_k). */
+rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int H, int rows, int head_dim,
+                                 const rehyat_mlp_weights* w, void* stream);
+
+/* Forward with the learned maps: the contract of rehyat_attn_fwd (causal != 0)
+ * or rehyat_attn_fwd_bidir (causal == 0), in dtype, with phi(q) = phi_q(q) and
+ * phi(k) = phi_k(k).  The per-device workspace also holds phi(q) and phi(k)
+ * (B H N 2 head_dim elements each). */
+rehyat_status rehyat_attn_fwd_mlp(const void* q, const void* k, const void* v, void* out, int dtype,
+                                  int B, int H, int frames, int tokens_per_frame, int head_dim,
+                                  int chunk_frames, int overlap_frames, int causal,
+                                  const rehyat_mlp_weights* phi_q, const rehyat_mlp_weights* phi_k,
+                                  void* stream);
+/* Per-query partials of the above (see rehyat_attn_fwd_partials). */
+rehyat_status rehyat_attn_fwd_mlp_partials(const void* q, const void* k, const void* v, int dtype,
+                                           float* m, float* nt, float* o_s, float* o_l, float* n_l,
+                                           int B, int H, int frames, int tokens_per_frame, int head_dim,
+                                           int chunk_frames, int overlap_frames, int causal,
+                                           const rehyat_mlp_weights* phi_q,
+                                           const rehyat_mlp_weights* phi_k, void* stream);
+/* One streaming step with the learned maps, on a state initialised with
+ * REHYAT_PHI_MLP2 (the state then also carries phi(k) of the overlap frames).
+ * The same weights must be passed on every step of a stream. */
+rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const void* k, const void* v,
+                                   void* out, int frames, const rehyat_mlp_weights* phi_q,
+                                   const rehyat_mlp_weights* phi_k, void* stream);
 
 /*
  * Profiling aid.  While set on the calling thread, every whole-clip forward

@@ -16,13 +16,13 @@ import ctypes
 import os
 
 __all__ = ["RehyatError", "attn_fwd", "attn_fwd_partials", "StepState", "feature_map_id",
-           "library_path", "load_library", "exported_symbols"]
+           "MlpWeights", "feature_mlp", "library_path", "load_library", "exported_symbols"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "librehyat.so")
 _lib = None
 
-FEATURE_MAPS = {"none": 0, "elu1": 1, "poly2": 2}
+FEATURE_MAPS = {"none": 0, "elu1": 1, "poly2": 2, "mlp2": 3}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every entry point declared in include/rehyat.h
@@ -30,6 +30,7 @@ exported_symbols = (
     "rehyat_attn_fwd", "rehyat_attn_fwd_f32", "rehyat_attn_fwd_partials",
     "rehyat_attn_fwd_bidir", "rehyat_attn_fwd_bidir_f32", "rehyat_attn_fwd_bidir_partials",
     "rehyat_step_state_bytes", "rehyat_step_state_init", "rehyat_attn_step",
+    "rehyat_feature_mlp", "rehyat_attn_fwd_mlp", "rehyat_attn_fwd_mlp_partials", "rehyat_attn_step_mlp",
     "rehyat_set_profile_events", "rehyat_status_string", "rehyat_last_error", "rehyat_version",
 )
 
@@ -49,6 +50,11 @@ class _StepStateC(ctypes.Structure):
         ("prev_frames", ctypes.c_int), ("prev_slot", ctypes.c_int), ("state_nonempty", ctypes.c_int),
         ("frames_done", ctypes.c_longlong),
     ]
+
+
+class _MlpC(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("hidden", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -78,6 +84,15 @@ def load_library():
     lib.rehyat_step_state_init.restype = i
     lib.rehyat_attn_step.argtypes = [ctypes.POINTER(_StepStateC), vp, vp, vp, vp, i, vp]
     lib.rehyat_attn_step.restype = i
+    mp = ctypes.POINTER(_MlpC)
+    lib.rehyat_feature_mlp.argtypes = [vp, vp, i, i, i, i, i, mp, vp]
+    lib.rehyat_feature_mlp.restype = i
+    lib.rehyat_attn_fwd_mlp.argtypes = [vp, vp, vp, vp] + [i] * 9 + [mp, mp, vp]
+    lib.rehyat_attn_fwd_mlp.restype = i
+    lib.rehyat_attn_fwd_mlp_partials.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp] + [i] * 8 + [mp, mp, vp]
+    lib.rehyat_attn_fwd_mlp_partials.restype = i
+    lib.rehyat_attn_step_mlp.argtypes = [ctypes.POINTER(_StepStateC), vp, vp, vp, vp, i, mp, mp, vp]
+    lib.rehyat_attn_step_mlp.restype = i
     lib.rehyat_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     lib.rehyat_set_profile_events.restype = i
     lib.rehyat_status_string.argtypes = [i]
@@ -136,12 +151,62 @@ def _check_qkv(q, k, v):
         raise RehyatError(1, "q, k, v must have the same shape and dtype")
 
 
+class MlpWeights:
+    """Weights of one learned feature map (include/rehyat.h, rehyat_mlp_weights):
+    w1 [H, hidden, d] and w2 [H, 2d, hidden] in the dtype of the calls they serve,
+    b1 [H, hidden] and b2 [H, 2d] in float32, all contiguous on the GPU."""
+
+    def __init__(self, w1, b1, w2, b2):
+        torch = _torch()
+        for name, t in (("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise RehyatError(1, f"{name} must be a contiguous GPU tensor")
+        if b1.dtype != torch.float32 or b2.dtype != torch.float32:
+            raise RehyatError(1, "b1 and b2 must be float32")
+        if w1.dim() != 3 or w2.dim() != 3 or w2.shape[2] != w1.shape[1] or w2.shape[1] != 2 * w1.shape[2]:
+            raise RehyatError(1, "expected w1 [H, hidden, d] and w2 [H, 2d, hidden]")
+        if tuple(b1.shape) != tuple(w1.shape[:2]) or tuple(b2.shape) != tuple(w2.shape[:2]):
+            raise RehyatError(1, "expected b1 [H, hidden] and b2 [H, 2d]")
+        self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
+        self.hidden = int(w1.shape[1])
+        self._c = _MlpC(w1.data_ptr(), b1.data_ptr(), w2.data_ptr(), b2.data_ptr(), self.hidden)
+
+    def check(self, x):
+        if self.w1.dtype != x.dtype or self.w1.shape[0] != x.shape[1] or self.w1.shape[2] != x.shape[3]:
+            raise RehyatError(1, "feature-map weights do not match the inputs (dtype, H or head_dim)")
+        return ctypes.byref(self._c)
+
+
+def _mlp_pair(feature_map):
+    """(phi_q, phi_k) if ``feature_map`` is a pair of MlpWeights, else None."""
+    if isinstance(feature_map, (tuple, list)):
+        if len(feature_map) != 2 or not all(isinstance(w, MlpWeights) for w in feature_map):
+            raise RehyatError(1, "a learned feature map is a pair (phi_q, phi_k) of MlpWeights")
+        return feature_map
+    return None
+
+
+def feature_mlp(x, weights, out=None, stream=None):
+    """phi of every row of x [B, H, rows, d] with one learned map -> [B, H, rows, 2d]."""
+    torch = _torch()
+    lib = load_library()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 4:
+        raise RehyatError(1, "x must be a contiguous [B, H, rows, d] GPU tensor")
+    B, H, R, d = x.shape
+    if out is None:
+        out = torch.empty(B, H, R, 2 * d, dtype=x.dtype, device=x.device)
+    _check(lib.rehyat_feature_mlp(x.data_ptr(), out.data_ptr(), _dtype_id(x), B, H, R, d, weights.check(x),
+                                  _stream_handle(stream)))
+    return out
+
+
 def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, feature_map="elu1",
              out=None, stream=None, causal=True):
     """Whole-clip hybrid attention forward.  q, k, v: [B, H, frames*tokens_per_frame, d]
     (bf16 or fp32, contiguous, on the GPU).  Returns ``out`` (allocated if None).
     causal=False selects the bidirectional form (keys of later chunks join the
-    linear set)."""
+    linear set).  ``feature_map`` is a name ("elu1", "poly2", "none") or a pair
+    (phi_q, phi_k) of MlpWeights (the learned map)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -152,6 +217,13 @@ def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, fe
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise RehyatError(1, "out must match q")
+    pair = _mlp_pair(feature_map)
+    if pair is not None:
+        _check(lib.rehyat_attn_fwd_mlp(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_id(q),
+                                       B, H, frames, tokens_per_frame, d, chunk_frames, overlap_frames,
+                                       1 if causal else 0, pair[0].check(q), pair[1].check(k),
+                                       _stream_handle(stream)))
+        return out
     bf16 = _dtype_id(q) == DTYPE_BF16
     if causal:
         fn = lib.rehyat_attn_fwd if bf16 else lib.rehyat_attn_fwd_f32
@@ -175,12 +247,17 @@ def attn_fwd_partials(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_f
     parts = {"m": torch.empty(B, H, N, **f32), "nt": torch.empty(B, H, N, **f32),
              "o_s": torch.empty(B, H, N, d, **f32), "o_l": torch.empty(B, H, N, d, **f32),
              "n_l": torch.empty(B, H, N, **f32)}
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_id(q),
+            parts["m"].data_ptr(), parts["nt"].data_ptr(), parts["o_s"].data_ptr(),
+            parts["o_l"].data_ptr(), parts["n_l"].data_ptr(), B, H, frames, tokens_per_frame, d,
+            chunk_frames, overlap_frames)
+    pair = _mlp_pair(feature_map)
+    if pair is not None:
+        _check(lib.rehyat_attn_fwd_mlp_partials(*ptrs, 1 if causal else 0, pair[0].check(q), pair[1].check(k),
+                                                _stream_handle(stream)))
+        return parts
     fn = lib.rehyat_attn_fwd_partials if causal else lib.rehyat_attn_fwd_bidir_partials
-    _check(fn(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_id(q),
-        parts["m"].data_ptr(), parts["nt"].data_ptr(), parts["o_s"].data_ptr(),
-        parts["o_l"].data_ptr(), parts["n_l"].data_ptr(), B, H, frames, tokens_per_frame, d,
-        chunk_frames, overlap_frames, feature_map_id(feature_map), _stream_handle(stream)))
+    _check(fn(*ptrs, feature_map_id(feature_map), _stream_handle(stream)))
     return parts
 
 
@@ -206,7 +283,8 @@ class StepState:
         dtype = torch.bfloat16 if dtype is None else dtype
         self.dtype = dtype
         did = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
-        fm = feature_map_id(feature_map)
+        self.mlp = _mlp_pair(feature_map)  # learned maps: passed again on every step
+        fm = FEATURE_MAPS["mlp2"] if self.mlp is not None else feature_map_id(feature_map)
         nbytes = lib.rehyat_step_state_bytes(B, H, tokens_per_frame, head_dim, chunk_frames,
                                              overlap_frames, fm, did)
         if nbytes == 0:  # invalid geometry: let init report why
@@ -243,6 +321,11 @@ class StepState:
             raise RehyatError(1, f"chunk rows {n} not a multiple of tokens_per_frame {HW}")
         if out is None:
             out = torch.empty_like(q)
+        if self.mlp is not None:
+            _check(lib.rehyat_attn_step_mlp(ctypes.byref(self._c), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            out.data_ptr(), n // HW, self.mlp[0].check(q), self.mlp[1].check(k),
+                                            _stream_handle(stream)))
+            return out
         _check(lib.rehyat_attn_step(ctypes.byref(self._c), q.data_ptr(), k.data_ptr(),
                                     v.data_ptr(), out.data_ptr(), n // HW, _stream_handle(stream)))
         return out

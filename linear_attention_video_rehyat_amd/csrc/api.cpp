@@ -78,14 +78,17 @@ struct Geometry {
 };
 
 rehyat_status check_common(Geometry& g, int B, int H, int frames, int tpf, int d, int Tc, int To,
-                           int phi, int dtype) {
+                           int phi, int dtype, bool mlp = false) {
     if (B < 1 || H < 1) return fail(REHYAT_EINVAL, "B and H must be >= 1 (got B=%d H=%d)", B, H);
     if (frames < 1 || tpf < 1)
         return fail(REHYAT_EINVAL, "frames and tokens_per_frame must be >= 1 (got %d, %d)", frames, tpf);
     if (Tc < 1) return fail(REHYAT_EINVAL, "chunk_frames must be >= 1 (got %d)", Tc);
     if (To < 0) return fail(REHYAT_EINVAL, "overlap_frames must be >= 0 (got %d)", To);
-    if (phi < REHYAT_PHI_NONE || phi > REHYAT_PHI_POLY2)
+    if (phi < REHYAT_PHI_NONE || phi > REHYAT_PHI_MLP2)
         return fail(REHYAT_EINVAL, "unknown feature_map %d", phi);
+    if ((phi == REHYAT_PHI_MLP2) != mlp)
+        return fail(REHYAT_EINVAL, mlp ? "internal: learned map without REHYAT_PHI_MLP2"
+                                       : "REHYAT_PHI_MLP2 needs its weights: use the _mlp entry points");
     if (dtype != REHYAT_F32 && dtype != REHYAT_BF16) return fail(REHYAT_EINVAL, "unknown dtype %d", dtype);
     if (dtype == REHYAT_BF16 && !bf16_dim_ok(d))
         return fail(REHYAT_EUNSUPPORTED, "head_dim %d not supported for bf16 (32, 64, 128)", d);
@@ -210,7 +213,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of the whole-clip forward: partial block sums and prepared states.
 struct FwdWorkspace {
-    size_t partial_off, shi_off, slo_off, z_off, suffix_off, total;
+    size_t partial_off, shi_off, slo_off, z_off, suffix_off, fq_off, fk_off, total;
     int U, n_sub;
     SubSplit split;
 };
@@ -233,7 +236,11 @@ FwdWorkspace fwd_workspace(const Geometry& g, int mode) {
     w.z_off = w.slo_off + (g.dtype == REHYAT_BF16 ? align256(sprep) : 0);
     w.suffix_off = w.z_off + align256(zprep);
     const size_t suffix = mode == kBidirectional ? (size_t)g.BH * g.C * g.E * 4 : 0;
-    w.total = w.suffix_off + align256(suffix);
+    // learned map: phi(q) and phi(k) rows, [BH][N][2d] each
+    const size_t feat = g.phi == REHYAT_PHI_MLP2 ? (size_t)g.BH * g.N * g.Dp * g.elem : 0;
+    w.fq_off = w.suffix_off + align256(suffix);
+    w.fk_off = w.fq_off + align256(feat);
+    w.total = w.fk_off + align256(feat);
     return w;
 }
 
@@ -246,8 +253,51 @@ bool any_linear(const Geometry& g, int mode) {
     return (long long)(g.C - 1) * g.Tc - g.To > 0;
 }
 
+// The learned feature map of rows [rq0, rq1) of x_q and [rk0, rk1) of x_k
+// (every (b, h)) into fq / fk, laid out like the inputs with 2d columns.
+hipError_t launch_mlp(const Geometry& g, const rehyat_mlp_weights* wq, const rehyat_mlp_weights* wk,
+                      const void* xq, void* fq, long long q_rows, int rq0, int rq1,
+                      const void* xk, void* fk, long long k_rows, int rk0, int rk1, hipStream_t s) {
+    MlpParams mp{};
+    const rehyat_mlp_weights* ws[2] = {wq, wk};
+    const void* xs[2] = {xq, xk};
+    void* os[2] = {fq, fk};
+    const long long rows[2] = {q_rows, k_rows};
+    const int r0[2] = {rq0, rk0}, r1[2] = {rq1, rk1};
+    for (int i = 0; i < 2; ++i) {
+        if (r1[i] <= r0[i]) continue;
+        MlpSide& sd = mp.side[mp.n_sides++];
+        sd.x = xs[i]; sd.out = os[i];
+        sd.w1 = ws[i]->w1; sd.b1 = ws[i]->b1; sd.w2 = ws[i]->w2; sd.b2 = ws[i]->b2;
+        sd.x_bh_stride = rows[i] * g.d; sd.out_bh_stride = rows[i] * g.Dp;
+        sd.r0 = r0[i]; sd.r1 = r1[i];
+    }
+    if (mp.n_sides == 0) return hipSuccess;
+    mp.BH = g.BH; mp.H = g.H; mp.d = g.d; mp.hidden = wq->hidden;
+    if (g.dtype == REHYAT_BF16) {
+        long long blocks = 0;
+        for (int i = 0; i < mp.n_sides; ++i) blocks += (long long)g.BH * ((mp.side[i].r1 - mp.side[i].r0 + 127) / 128);
+        mp.grid = (int)std::min<long long>(blocks, 8LL * cus_per_xcd());
+        return launch_phi_mlp_bf16(mp, s);
+    }
+    return launch_phi_mlp_f32(mp, s);
+}
+
+// Query rows whose chunk has a linear set, and key rows in some linear set.
+void mlp_rows(const Geometry& g, int mode, int& q0, int& k1) {
+    if (mode == kBidirectional) {
+        q0 = 0;
+        k1 = (int)g.N;
+        return;
+    }
+    const long long t_min = g.To / g.Tc + 1;  // first chunk with t T_c - T_o > 0
+    q0 = (int)(std::min<long long>(t_min * g.Tc, g.F) * g.HW);
+    k1 = (int)(std::max<long long>((long long)(g.C - 1) * g.Tc - g.To, 0) * g.HW);
+}
+
 rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g, int mode,
-                      float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s) {
+                      float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s,
+                      const rehyat_mlp_weights* wq = nullptr, const rehyat_mlp_weights* wk = nullptr) {
     const bool lin = any_linear(g, mode);
     char* ws = nullptr;
     FwdWorkspace w{};
@@ -259,6 +309,12 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         rehyat_status st = arena_get(w.total, &p);
         if (st != REHYAT_OK) return st;
         ws = (char*)p;
+        if (g.phi == REHYAT_PHI_MLP2) {
+            int q0 = 0, k1 = 0;
+            mlp_rows(g, mode, q0, k1);
+            hipError_t e = launch_mlp(g, wq, wk, q, ws + w.fq_off, g.N, q0, (int)g.N, k, ws + w.fk_off, g.N, 0, k1, s);
+            if (e != hipSuccess) return hip_fail(e, "feature-map launch");
+        }
 
         StateParams sp{};
         sp.k = k; sp.v = v; sp.kp = nullptr; sp.vp = nullptr;
@@ -268,6 +324,10 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
         sp.mode = mode; sp.F = g.F;
         sp.partial = (float*)(ws + w.partial_off);
+        if (g.phi == REHYAT_PHI_MLP2) {
+            sp.fk = ws + w.fk_off; sp.fk_bh_stride = g.N * g.Dp;
+            sp.fkp = nullptr; sp.fkp_bh_stride = 0;
+        }
         hipError_t e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         if ((e = prof_mark(1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -303,6 +363,10 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         lp.s_hi = ws + w.shi_off; lp.s_lo = ws + w.slo_off; lp.z = (const float*)(ws + w.z_off);
         lp.s_chunk_stride = (long long)g.d * g.Dp; lp.s_bh_stride = (long long)g.C * g.d * g.Dp;
         lp.z_chunk_stride = g.Dp; lp.z_bh_stride = (long long)g.C * g.Dp;
+        if (g.phi == REHYAT_PHI_MLP2) {
+            lp.fq = ws + w.fq_off;
+            lp.fq_bh_stride = g.N * g.Dp;
+        }
     } else {
         lp.phi = REHYAT_PHI_NONE;  // no chunk has a linear set
     }
@@ -313,12 +377,32 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
     return REHYAT_OK;
 }
 
+// Weights of the learned query and key maps: present, 16-byte aligned, and a
+// hidden width the kernels are built for (the same for both maps).
+rehyat_status check_mlp(const rehyat_mlp_weights* wq, const rehyat_mlp_weights* wk) {
+    if (!wq || !wk) return fail(REHYAT_EINVAL, "null feature-map weights");
+    for (const rehyat_mlp_weights* w : {wq, wk}) {
+        if (!w->w1 || !w->b1 || !w->w2 || !w->b2) return fail(REHYAT_EINVAL, "null feature-map weight pointer");
+        if (!aligned16(w->w1) || !aligned16(w->b1) || !aligned16(w->w2) || !aligned16(w->b2))
+            return fail(REHYAT_EINVAL, "feature-map weights must be 16-byte aligned");
+        if (!phi_mlp_hidden_ok(w->hidden))
+            return fail(REHYAT_EUNSUPPORTED, "feature-map hidden width %d not supported (32, 64, 128, 256)", w->hidden);
+    }
+    if (wq->hidden != wk->hidden)
+        return fail(REHYAT_EUNSUPPORTED, "query and key maps must have the same hidden width (%d vs %d)",
+                    wq->hidden, wk->hidden);
+    return REHYAT_OK;
+}
+
 rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, int B, int H,
                         int frames, int tpf, int d, int Tc, int To, int phi, int dtype, int mode,
-                        void* stream) {
+                        void* stream, const rehyat_mlp_weights* wq = nullptr,
+                        const rehyat_mlp_weights* wk = nullptr) {
     Geometry g{};
-    rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
+    const bool mlp = phi == REHYAT_PHI_MLP2 && (wq || wk);
+    rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype, mlp);
     if (st != REHYAT_OK) return st;
+    if (mlp && (st = check_mlp(wq, wk)) != REHYAT_OK) return st;
     if (!q || !k || !v || !out) return fail(REHYAT_EINVAL, "null tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(REHYAT_EINVAL, "tensor pointers must be 16-byte aligned");
@@ -326,27 +410,31 @@ rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, 
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
         return fail(REHYAT_EINVAL, "out must not overlap q, k or v");
     g_last_error.clear();
-    return run_fwd(q, k, v, out, g, mode, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream);
+    return run_fwd(q, k, v, out, g, mode, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream, wq, wk);
 }
 
 rehyat_status partials_entry(const void* q, const void* k, const void* v, int dtype, float* m, float* nt,
                              float* o_s, float* o_l, float* n_l, int B, int H, int frames, int tpf, int d,
-                             int Tc, int To, int phi, int mode, void* stream) {
+                             int Tc, int To, int phi, int mode, void* stream,
+                             const rehyat_mlp_weights* wq = nullptr, const rehyat_mlp_weights* wk = nullptr) {
     Geometry g{};
-    rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
+    const bool mlp = phi == REHYAT_PHI_MLP2 && (wq || wk);
+    rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype, mlp);
     if (st != REHYAT_OK) return st;
+    if (mlp && (st = check_mlp(wq, wk)) != REHYAT_OK) return st;
     if (!q || !k || !v) return fail(REHYAT_EINVAL, "null tensor pointer");
     if (!m && !nt && !o_s && !o_l && !n_l) return fail(REHYAT_EINVAL, "no partial output requested");
     const void* ptrs[8] = {q, k, v, m, nt, o_s, o_l, n_l};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(REHYAT_EINVAL, "pointers must be 16-byte aligned");
     g_last_error.clear();
-    return run_fwd(q, k, v, nullptr, g, mode, m, nt, o_s, o_l, n_l, (hipStream_t)stream);
+    return run_fwd(q, k, v, nullptr, g, mode, m, nt, o_s, o_l, n_l, (hipStream_t)stream, wq, wk);
 }
 
 // ---------------------------------------------------------------- streaming state
 struct StepLayout {
     size_t S_off, shi_off, slo_off, z_off, kp_off[2], vp_off[2], partial_off, total;
+    size_t fq_off, fk_off, fkp_off[2];  // learned map: phi rows of the chunk and of the overlap frames
     int n_sub;
     size_t prev_bytes;  // one K (or V) slot
 };
@@ -368,6 +456,16 @@ StepLayout step_layout(const Geometry& g) {
         L.vp_off[i] = off; off += align256(L.prev_bytes);
     }
     L.partial_off = off; off += align256((size_t)g.BH * L.n_sub * E * 4);
+    if (g.phi == REHYAT_PHI_MLP2) {
+        const size_t chunk_feat = (size_t)g.BH * g.Tc * g.HW * g.Dp * g.elem;
+        const size_t prev_feat = (size_t)g.BH * g.To * g.HW * g.Dp * g.elem;
+        L.fq_off = off; off += align256(chunk_feat);
+        L.fk_off = off; off += align256(chunk_feat);
+        for (int i = 0; i < 2; ++i) {
+            L.fkp_off[i] = off;
+            off += align256(prev_feat);
+        }
+    }
     L.total = off > 256 ? off : 256;  // never 0: 0 means "invalid arguments"
     return L;
 }
@@ -428,7 +526,7 @@ size_t rehyat_step_state_bytes(int B, int H, int tokens_per_frame, int head_dim,
                                int overlap_frames, int feature_map, int dtype) {
     Geometry g{};
     if (check_common(g, B, H, chunk_frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
-                     feature_map, dtype) != REHYAT_OK)
+                     feature_map, dtype, feature_map == REHYAT_PHI_MLP2) != REHYAT_OK)
         return 0;
     return step_layout(g).total;
 }
@@ -439,7 +537,7 @@ rehyat_status rehyat_step_state_init(rehyat_step_state* st, void* buf, size_t by
     if (!st) return fail(REHYAT_EINVAL, "null state");
     Geometry g{};
     rehyat_status s = check_common(g, B, H, chunk_frames, tokens_per_frame, head_dim, chunk_frames,
-                                   overlap_frames, feature_map, dtype);
+                                   overlap_frames, feature_map, dtype, feature_map == REHYAT_PHI_MLP2);
     if (s != REHYAT_OK) return s;
     const size_t need = step_layout(g).total;
     if (!buf) return fail(REHYAT_EINVAL, "null state buffer");
@@ -455,14 +553,19 @@ rehyat_status rehyat_step_state_init(rehyat_step_state* st, void* buf, size_t by
     return REHYAT_OK;
 }
 
-rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void* k, const void* v,
-                               void* out, int frames, void* stream) {
+static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void* k, const void* v, void* out,
+                               int frames, void* stream, const rehyat_mlp_weights* wq,
+                               const rehyat_mlp_weights* wk) {
     if (!st || !st->buf) return fail(REHYAT_EINVAL, "state not initialised");
     Geometry g{};
+    const bool mlp = wq != nullptr;
+    if (mlp && st->feature_map != REHYAT_PHI_MLP2)
+        return fail(REHYAT_EINVAL, "the state was not initialised for REHYAT_PHI_MLP2");
     rehyat_status s0 = check_common(g, st->B, st->H, st->chunk_frames, st->tokens_per_frame,
                                     st->head_dim, st->chunk_frames, st->overlap_frames,
-                                    st->feature_map, st->dtype);
+                                    st->feature_map, st->dtype, mlp);
     if (s0 != REHYAT_OK) return s0;
+    if (mlp && (s0 = check_mlp(wq, wk)) != REHYAT_OK) return s0;
     const StepLayout L = step_layout(g);
     if (st->bytes < L.total) return fail(REHYAT_EINVAL, "state buffer too small");
     if (frames < 1 || frames > st->chunk_frames)
@@ -484,6 +587,10 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
     char* base = (char*)st->buf;
     const int P = st->prev_frames * g.HW;
     const int cur = st->prev_slot;
+    if (mlp) {  // phi of the chunk's queries and keys (the overlap frames' phi(k) is carried)
+        hipError_t e = launch_mlp(g, wq, wk, q, base + L.fq_off, n, 0, (int)n, k, base + L.fk_off, n, 0, (int)n, s);
+        if (e != hipSuccess) return hip_fail(e, "feature-map launch");
+    }
 
     // 1. local softmax over [prev | chunk] + linear branch from the carried state
     LocalParams lp{};
@@ -503,6 +610,10 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
     lp.s_hi = base + L.shi_off; lp.s_lo = base + L.slo_off; lp.z = (const float*)(base + L.z_off);
     lp.s_chunk_stride = 0; lp.s_bh_stride = (long long)g.d * g.Dp;
     lp.z_chunk_stride = 0; lp.z_bh_stride = g.Dp;
+    if (mlp) {
+        lp.fq = base + L.fq_off;
+        lp.fq_bh_stride = n * g.Dp;
+    }
     hipError_t e = g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s);
     if (e != hipSuccess) return hip_fail(e, "local-attention launch");
 
@@ -525,6 +636,10 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi;
         sp.mode = kCausal; sp.F = frames;
         sp.partial = (float*)(base + L.partial_off);
+        if (mlp) {
+            sp.fk = base + L.fk_off; sp.fk_bh_stride = n * g.Dp;
+            sp.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; sp.fkp_bh_stride = (long long)g.To * g.HW * g.Dp;
+        }
         e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         ScanParams cp{};
@@ -548,6 +663,10 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
         pc.k = k; pc.v = v; pc.bh_stride = n * g.d; pc.chunk_rows = (int)n;
         pc.kd = base + L.kp_off[cur ^ 1]; pc.vd = base + L.vp_off[cur ^ 1];
         pc.keep_rows = keep_rows; pc.BH = g.BH; pc.d = g.d; pc.elem_bytes = g.elem;
+        if (mlp) {
+            pc.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; pc.fk = base + L.fk_off; pc.fkd = base + L.fkp_off[cur ^ 1];
+            pc.fprev_bh_stride = (long long)g.To * g.HW * g.Dp; pc.f_bh_stride = n * g.Dp; pc.f_cols = g.Dp;
+        }
         e = launch_prev_copy(pc, s);
         if (e != hipSuccess) return hip_fail(e, "overlap copy launch");
     }
@@ -556,6 +675,53 @@ rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void*
     st->state_nonempty = nonempty ? 1 : 0;
     st->frames_done = done;
     return REHYAT_OK;
+}
+
+rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void* k, const void* v,
+                               void* out, int frames, void* stream) {
+    return step_impl(st, q, k, v, out, frames, stream, nullptr, nullptr);
+}
+
+rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const void* k, const void* v,
+                                   void* out, int frames, const rehyat_mlp_weights* phi_q,
+                                   const rehyat_mlp_weights* phi_k, void* stream) {
+    if (!phi_q || !phi_k) return fail(REHYAT_EINVAL, "null feature-map weights");
+    return step_impl(st, q, k, v, out, frames, stream, phi_q, phi_k);
+}
+
+rehyat_status rehyat_attn_fwd_mlp(const void* q, const void* k, const void* v, void* out, int dtype, int B,
+                                  int H, int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+                                  int overlap_frames, int causal, const rehyat_mlp_weights* phi_q,
+                                  const rehyat_mlp_weights* phi_k, void* stream) {
+    if (!phi_q || !phi_k) return fail(REHYAT_EINVAL, "null feature-map weights");
+    return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
+                     REHYAT_PHI_MLP2, dtype, causal ? kCausal : kBidirectional, stream, phi_q, phi_k);
+}
+
+rehyat_status rehyat_attn_fwd_mlp_partials(const void* q, const void* k, const void* v, int dtype, float* m,
+                                           float* nt, float* o_s, float* o_l, float* n_l, int B, int H,
+                                           int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+                                           int overlap_frames, int causal, const rehyat_mlp_weights* phi_q,
+                                           const rehyat_mlp_weights* phi_k, void* stream) {
+    if (!phi_q || !phi_k) return fail(REHYAT_EINVAL, "null feature-map weights");
+    return partials_entry(q, k, v, dtype, m, nt, o_s, o_l, n_l, B, H, frames, tokens_per_frame, head_dim,
+                          chunk_frames, overlap_frames, REHYAT_PHI_MLP2, causal ? kCausal : kBidirectional,
+                          stream, phi_q, phi_k);
+}
+
+rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int H, int rows, int head_dim,
+                                 const rehyat_mlp_weights* w, void* stream) {
+    Geometry g{};
+    rehyat_status st = check_common(g, B, H, 1, rows, head_dim, 1, 0, REHYAT_PHI_MLP2, dtype, true);
+    if (st != REHYAT_OK) return st;
+    if ((st = check_mlp(w, w)) != REHYAT_OK) return st;
+    if (!x || !phi) return fail(REHYAT_EINVAL, "null tensor pointer");
+    if (!aligned16(x) || !aligned16(phi)) return fail(REHYAT_EINVAL, "tensor pointers must be 16-byte aligned");
+    const size_t xb = (size_t)g.BH * rows * head_dim * g.elem, pb = 2 * xb;
+    if (overlaps(x, xb, phi, pb)) return fail(REHYAT_EINVAL, "phi must not overlap x");
+    g_last_error.clear();
+    hipError_t e = launch_mlp(g, w, w, x, phi, rows, 0, rows, nullptr, nullptr, 0, 0, 0, (hipStream_t)stream);
+    return e == hipSuccess ? REHYAT_OK : hip_fail(e, "feature-map launch");
 }
 
 rehyat_status rehyat_set_profile_events(void* const* events, int n_events) {

@@ -17,7 +17,7 @@ constexpr int kF32Rows = 128;  // queries per workgroup (one per lane)
 template <int D, int PHI>
 __global__ __launch_bounds__(kF32Rows) void local_f32_kernel(LocalParams p) {
     constexpr int BN = 32;
-    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     __shared__ __attribute__((aligned(16))) float Ks[BN][D];
     __shared__ __attribute__((aligned(16))) float Vs[BN][D];
 
@@ -101,9 +101,10 @@ __global__ __launch_bounds__(kF32Rows) void local_f32_kernel(LocalParams p) {
     if (PHI != kPhiNone && lin) {
         const float* st = (const float*)p.s_hi + bh * p.s_bh_stride + t * p.s_chunk_stride;
         const float* zp = p.z + bh * p.z_bh_stride + t * p.z_chunk_stride;
+        const float* fqr = PHI == kPhiFeat ? (const float*)p.fq + bh * p.fq_bh_stride + (long long)rowc * DP : nullptr;
         for (int c = 0; c < DP; ++c) {
             const float x = q[c % D];
-            const float f = c < D ? (x > 0.0f ? x + 1.0f : expf(x)) : x * x;
+            const float f = PHI == kPhiFeat ? fqr[c] : (c < D ? (x > 0.0f ? x + 1.0f : expf(x)) : x * x);
             nl = fmaf(f, zp[c], nl);
 #pragma unroll
             for (int dd = 0; dd < D; ++dd) al[dd] = fmaf(f, st[(long long)dd * DP + c], al[dd]);
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kF32Rows) void local_f32_kernel(LocalParams p) {
 template <int D, int PHI>
 __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
     constexpr int BN = 32;
-    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     constexpr int SE = D * DP;
     constexpr int PER = (SE + 255) / 256;
     __shared__ float Fs[BN][DP];
@@ -174,6 +175,8 @@ __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
     const float* vb = (const float*)p.v + bh * p.bh_stride;
     const float* kpb = p.kp ? (const float*)p.kp + bh * p.prev_bh_stride : nullptr;
     const float* vpb = p.vp ? (const float*)p.vp + bh * p.prev_bh_stride : nullptr;
+    const float* fkb = PHI == kPhiFeat ? (const float*)p.fk + bh * p.fk_bh_stride : nullptr;
+    const float* fkpb = PHI == kPhiFeat && p.fkp ? (const float*)p.fkp + bh * p.fkp_bh_stride : nullptr;
 
     float acc[PER];
 #pragma unroll
@@ -187,15 +190,25 @@ __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
             if (j < j1) {
                 const float* ks = j < p.prev_rows ? kpb + (long long)j * D : kb + (long long)(j - p.prev_rows) * D;
                 const float* vs = j < p.prev_rows ? vpb + (long long)j * D : vb + (long long)(j - p.prev_rows) * D;
-                kv = ks[c];
+                kv = PHI == kPhiFeat ? 0.0f : ks[c];
                 vv = vs[c];
-                Fs[r][c] = kv > 0.0f ? kv + 1.0f : expf(kv);
+                if (PHI != kPhiFeat) Fs[r][c] = kv > 0.0f ? kv + 1.0f : expf(kv);
                 if (PHI == kPhiPoly2) Fs[r][D + c] = kv * kv;
             } else {
-                Fs[r][c] = 0.0f;
+                if (PHI != kPhiFeat) Fs[r][c] = 0.0f;
                 if (PHI == kPhiPoly2) Fs[r][D + c] = 0.0f;
             }
             Vs[r][c] = vv;
+        }
+        if (PHI == kPhiFeat) {  // precomputed phi(k) rows
+            for (int x = tid; x < BN * DP; x += 256) {
+                const int r = x / DP, c = x % DP;
+                const int j = base + r;
+                float f = 0.0f;
+                if (j < j1)
+                    f = j < p.prev_rows ? fkpb[(long long)j * DP + c] : fkb[(long long)(j - p.prev_rows) * DP + c];
+                Fs[r][c] = f;
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -231,6 +244,7 @@ hipError_t launch_local_d(const LocalParams& p, hipStream_t s) {
     case kPhiNone: local_f32_kernel<D, kPhiNone><<<blocks, kF32Rows, 0, s>>>(p); break;
     case kPhiElu1: local_f32_kernel<D, kPhiElu1><<<blocks, kF32Rows, 0, s>>>(p); break;
     case kPhiPoly2: local_f32_kernel<D, kPhiPoly2><<<blocks, kF32Rows, 0, s>>>(p); break;
+    case kPhiFeat: local_f32_kernel<D, kPhiFeat><<<blocks, kF32Rows, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -243,6 +257,7 @@ hipError_t launch_state_d(const StateParams& p, hipStream_t s) {
     switch (p.phi) {
     case kPhiElu1: state_f32_kernel<D, kPhiElu1><<<blocks, 256, 0, s>>>(p); break;
     case kPhiPoly2: state_f32_kernel<D, kPhiPoly2><<<blocks, 256, 0, s>>>(p); break;
+    case kPhiFeat: state_f32_kernel<D, kPhiFeat><<<blocks, 256, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

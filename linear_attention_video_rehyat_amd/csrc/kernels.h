@@ -7,9 +7,13 @@
 
 namespace rehyat {
 
-enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiPoly2 = 2 };
+// kPhiFeat: phi(q) and phi(k) come precomputed in feature buffers of D' = 2d
+// columns (the learned map, see MlpParams) instead of being applied to q and k.
+enum Phi { kPhiNone = 0, kPhiElu1 = 1, kPhiPoly2 = 2, kPhiFeat = 3 };
 
-inline int feature_dim(int phi, int d) { return phi == kPhiElu1 ? d : (phi == kPhiPoly2 ? 2 * d : 0); }
+inline int feature_dim(int phi, int d) {
+    return phi == kPhiElu1 ? d : ((phi == kPhiPoly2 || phi == kPhiFeat) ? 2 * d : 0);
+}
 
 // Partition of the keys into the blocks whose linear sums the state pass forms
 // (frame ranges, times tokens_per_frame for rows).
@@ -75,6 +79,9 @@ struct LocalParams {
     // optional partials (verification aid): fp32
     float* pm; float* pnt; float* poS; float* poL; float* pnL;
     int lpt_order;            // dispatch each XCD's work items longest first (see local_work_item)
+    // kPhiFeat: phi(q) rows, [BH][n_rows][2d] in the input dtype (row = query row)
+    const void* fq;
+    long long fq_bh_stride;
 };
 
 // Key tiles of BN keys that a query tile of chunk t streams (its softmax window).
@@ -136,6 +143,10 @@ struct StateParams {
     int BH, d, phi;
     int mode, F;                      // block partition (BlockMode) and frames of the clip
     float* partial;                   // [BH][U][n_sub][d*D' + D']
+    // kPhiFeat: phi(k) rows in the input dtype, [BH][n_rows][2d] and for the
+    // overlap segment [BH][prev rows][2d] (indexed like k and kp)
+    const void* fk; const void* fkp;
+    long long fk_bh_stride, fkp_bh_stride;
 };
 
 // Scan: X_0 = init (or 0); X_{u+1} = X_u + sum_p partial[u][p].  Writes the
@@ -157,12 +168,36 @@ struct ScanParams {
     float* suffix;                    // [BH][C][E] fp32 scratch for the suffix sums
 };
 
-// Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot.
+// Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot
+// (K, V and, for the learned map, phi(K) rows of f_cols columns).
 struct PrevCopyParams {
     const void* kp; const void* vp; long long prev_bh_stride; int prev_rows;
     const void* k; const void* v; long long bh_stride; int chunk_rows;
     void* kd; void* vd;               // destination slot, same stride as prev
     int keep_rows, BH, d, elem_bytes;
+    const void* fkp; const void* fk; void* fkd;   // phi(K) rows or null
+    long long fprev_bh_stride, f_bh_stride;
+    int f_cols;
+};
+
+// Learned feature map (ReHyAt §3.2 polynomial form with a two-layer MLP, §4.3 /
+// appendix §7.1): for every row x of the selected rows,
+//   psi = W2 relu(W1 x + b1) + b2   (2d values),  phi(x) = [1 + elu(psi[0:d]), psi[d:2d]^2],
+// per head, with separate weights for queries and keys (one "side" each).
+struct MlpSide {
+    const void* x;                    // [BH][.][d] rows in the input dtype
+    void* out;                        // [BH][.][2d] phi rows, input dtype; row r of x -> row r of out
+    const void* w1;                   // [H][hidden][d], input dtype
+    const float* b1;                  // [H][hidden]
+    const void* w2;                   // [H][2d][hidden], input dtype
+    const float* b2;                  // [H][2d]
+    long long x_bh_stride, out_bh_stride;  // elements between consecutive (b, h)
+    int r0, r1;                       // rows [r0, r1) of every (b, h) are mapped
+};
+struct MlpParams {
+    MlpSide side[2];
+    int n_sides, BH, H, d, hidden;
+    int grid;                         // workgroups (bf16 kernel: at most one per CU)
 };
 
 hipError_t launch_local_bf16(const LocalParams& p, hipStream_t s);
@@ -171,6 +206,9 @@ hipError_t launch_state_bf16(const StateParams& p, hipStream_t s);
 hipError_t launch_state_f32(const StateParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s);
+hipError_t launch_phi_mlp_bf16(const MlpParams& p, hipStream_t s);
+hipError_t launch_phi_mlp_f32(const MlpParams& p, hipStream_t s);
+bool phi_mlp_hidden_ok(int hidden);  // hidden widths the MLP kernels are built for
 
 int local_bf16_tile_rows(int d);   // queries per workgroup of the bf16 local kernel
 int local_bf16_key_tile(int d);    // keys per LDS tile of the bf16 local kernel

@@ -72,8 +72,6 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     constexpr int DT = D / 32;                   // 32-row tiles over head_dim
     constexpr int KT = BN / 32;                  // 32-key tiles per LDS tile
     constexpr int BM = NW * QB * 32;
-    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
-    constexpr int KSL = DP / 16;                 // k-steps over the feature dimension
     constexpr int NINST = BN * C / 64;           // 64-lane DMA instructions per K (or V) tile
     constexpr int OPS = 2 * NINST;               // per tile, K and V
     constexpr int OPW = (OPS + NW - 1) / NW;     // per wave
@@ -360,6 +358,7 @@ hipError_t launch_d(const LocalParams& p, hipStream_t s) {
     case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone, kStages><<<grid, block, 0, s>>>(p); break;
     case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1, kStages><<<grid, block, 0, s>>>(p); break;
     case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2, kStages><<<grid, block, 0, s>>>(p); break;
+    case kPhiFeat: local_bf16_kernel<D, QB, NW, BN, kPhiFeat, kStages><<<grid, block, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

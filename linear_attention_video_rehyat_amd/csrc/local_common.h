@@ -17,13 +17,14 @@ constexpr unsigned kVmcntBase = 0x0F70;
 constexpr unsigned vm_wait_imm(int n) { return kVmcntBase | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
 
 // XOR swizzle of the 16-byte chunks of row r of an unpadded tile with C chunks
-// per row (C = head_dim / 8).  Chosen so that (a) 16 consecutive rows read at
+// per row (C = head_dim / 8, or D' / 8).  Chosen so that (a) 16 consecutive rows read at
 // one logical chunk hit 16 different 4-bank groups (K fragment reads), and (b)
 // 4 consecutive rows read at 4 consecutive logical chunks (a transposing V
 // read) land in 4 different 16-bank groups.  It depends on r mod 16 only.
 template <int C>
 __device__ __forceinline__ int swz(int r) {
-    if constexpr (C == 16) return 4 * (r & 3) + ((r >> 2) & 3);
+    // rows of 16 or more chunks: every row starts in the same 4-bank group
+    if constexpr (C >= 16) return 4 * (r & 3) + ((r >> 2) & 3);
     else if constexpr (C == 8) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
     else return (r >> 2) & 3;
 }
@@ -37,15 +38,6 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Epilogue for one block of 32 queries (lane: query lq, half h of the keys).
-// oacc holds O^T of the softmax branch scaled by 2^-m2 (log2 domain), msum the
-// lane's share of the row sum at the same scale.  When `lin`, the linear
-// branch a^L = phi(q)^T S_t, n^L = phi(q).z_t is formed with a three-pass bf16
-// split of both MFMA operands (S_t comes prepared as bf16 hi + lo parts) and
-// n^L in fp32, and the two branches are combined as
-//   y = (2^-M2' a^S + 2^-M2 a^L) / (2^-M2' n^S + 2^-M2 n^L),  M2 = max(m2, log2 n^L),
-// which equals (a^S + a^L)/(n^S + n^L) exactly and stays finite in fp32.
-// Writes y in bf16, or the per-branch partials when any partial buffer is set.
 // Global->LDS copy of the prepared state S_t^T (bf16 hi part at dst, lo part
 // right after it, each [D][DP] row-major with the 16-byte chunks of row r
 // XOR-swizzled by swz(r)), spread over the NW waves of a workgroup.
@@ -72,20 +64,40 @@ __device__ __forceinline__ void issue_state_dma(lds_u16* dst, int wave, int lane
     }
 }
 
+// Epilogue for one block of 32 queries (lane: query lq, half h of the keys).
+// oacc holds O^T of the softmax branch scaled by 2^-m2 (log2 domain), msum the
+// lane's share of the row sum at the same scale.  When `lin`, the linear
+// branch a^L = phi(q)^T S_t, n^L = phi(q).z_t is formed with a three-pass bf16
+// split of both MFMA operands (S_t comes prepared as bf16 hi + lo parts; a
+// precomputed bf16 phi(q) has no lo part, so two passes) and
+// n^L in fp32, and the two branches are combined as
+//   y = (2^-M2' a^S + 2^-M2 a^L) / (2^-M2' n^S + 2^-M2 n^L),  M2 = max(m2, log2 n^L),
+// which equals (a^S + a^L)/(n^S + n^L) exactly and stays finite in fp32.
+// Writes y in bf16, or the per-branch partials when any partial buffer is set.
 template <int D, int PHI>
 __device__ __forceinline__ void finish_query_block(const LocalParams& p, const bf16x8 (&q)[D / 16],
                                                    const f32x16 (&oacc)[D / 32], float msum, float m2,
                                                    float mtrue, int row, int q_end, int bh, int t, int h,
                                                    int lq, bool lin, const lds_u16* s_lds = nullptr) {
     constexpr int KS = D / 16, DT = D / 32;
-    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
+    constexpr bool FEAT = PHI == kPhiFeat;  // phi(q) precomputed in bf16: no lo part
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     constexpr int KSL = PHI == kPhiNone ? 1 : DP / 16;
     const float lsum = xhalf_sum(msum);
     lin = PHI != kPhiNone && lin;
     // phi(q): n^L in fp32 and the bf16 hi/lo MFMA operands, kept in registers
     // unless there are too many of them (then formed again per output slice)
     constexpr bool KEEP = KSL <= 8;
+    const uint16_t* fqrow =
+        FEAT ? (const uint16_t*)p.fq + bh * p.fq_bh_stride + (long long)min(row, q_end - 1) * DP + 8 * h : nullptr;
     auto phi_frag = [&](int ksl, bf16x8& fh, bf16x8& fl, float* f) {
+        if constexpr (FEAT) {
+            const u32x4 w = ldg_b128(fqrow + 16 * ksl);
+            unpack8(w, f);
+            fh = __builtin_bit_cast(bf16x8, w);
+            fl = bf16x8{};
+            return;
+        }
         float x[8];
         unpack8(__builtin_bit_cast(u32x4, q[ksl % KS]), x);
 #pragma unroll
@@ -172,7 +184,7 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
                 }
                 lacc = mfma32x32x16(ahi, fh, lacc);
                 lacc = mfma32x32x16(alo, fh, lacc);
-                lacc = mfma32x32x16(ahi, fl, lacc);
+                if (!FEAT) lacc = mfma32x32x16(ahi, fl, lacc);
             }
         }
         if (!valid) continue;

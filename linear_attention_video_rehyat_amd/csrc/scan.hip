@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void prev_copy_kernel(PrevCopyParams p) {
     }
     const long long doff = ((long long)bh * p.prev_bh_stride) * p.elem_bytes + r * rowb + 16LL * c;
     *(u32x4*)((char*)p.kd + doff) = *(const u32x4*)(ks + 16LL * c);
-    *(u32x4*)((char*)p.vd + doff) = *(const u32x4*)(vs + 16LL * c);
+    if (p.vd) *(u32x4*)((char*)p.vd + doff) = *(const u32x4*)(vs + 16LL * c);
 }
 
 }  // namespace
@@ -143,6 +143,14 @@ hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s) {
     if (total <= 0) return hipSuccess;
     const long long blocks = (total + 255) / 256;
     prev_copy_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(p);
+    if (!p.fkd) return hipGetLastError();
+    // the phi(K) rows of the same frames, as a plane of their own
+    PrevCopyParams f = p;
+    f.kp = p.fkp; f.k = p.fk; f.kd = p.fkd;
+    f.vp = nullptr; f.v = nullptr; f.vd = nullptr;
+    f.prev_bh_stride = p.fprev_bh_stride; f.bh_stride = p.f_bh_stride; f.d = p.f_cols;
+    const long long ftotal = (long long)p.BH * p.keep_rows * (f.d * p.elem_bytes / 16);
+    prev_copy_kernel<<<dim3((unsigned)((ftotal + 255) / 256)), 256, 0, s>>>(f);
     return hipGetLastError();
 }
 

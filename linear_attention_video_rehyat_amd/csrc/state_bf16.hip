@@ -40,26 +40,28 @@ constexpr int state_waves(int dp) { return dp / 32 == 1 ? 4 : 8; }
 #endif
 constexpr int kStateStages = REHYAT_STATE_STAGES;
 
-// One wave's share of the global->LDS loads of a K/V tile (OPS instructions of
-// 1 KB: the first NINST fill the K tile, the rest the V tile).  Virtual key j <
-// prev_rows reads the overlap segment, the others read the clip at row
-// j - prev_rows.  Rows past a resource's end read as zero.
-template <int D, int BN, int NW, int OPW, int NINST>
+// One wave's share of the global->LDS loads of a K/V tile (instructions of 1
+// KB: the first NK fill the K tile, KW columns wide -- the keys, or their
+// precomputed features -- and the next NV the V tile, D columns wide).
+// Virtual key j < prev_rows reads the overlap segment, the others read the
+// clip at row j - prev_rows.  Rows past a resource's end read as zero.
+template <int D, int KW, int BN, int NW, int OPW>
 __device__ __forceinline__ void state_load_tile(lds_u16* base, int wave, int lane, int j0, int prev_rows,
                                                 __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                                 __amdgpu_buffer_rsrc_t kprs, __amdgpu_buffer_rsrc_t vprs) {
-    constexpr int C = D / 8;
-    constexpr int rb = D * 2;
+    constexpr int NK = BN * KW / 512;
 #pragma unroll
     for (int o = 0; o < OPW; ++o) {
         const int op = wave + o * NW;
-        const bool isv = op >= NINST;
-        const int ins = op % NINST;
+        const bool isv = op >= NK;
+        const int ins = isv ? op - NK : op;
         const int pos = 64 * ins + lane;
+        const int C = isv ? D / 8 : KW / 8;  // uniform per instruction
         const int r = pos / C;
-        const int c16 = ((pos % C) ^ swz<C>(r)) * 16;
+        const int c16 = ((pos % C) ^ (isv ? swz<D / 8>(r) : swz<KW / 8>(r))) * 16;
+        const int rb = isv ? D * 2 : KW * 2;
         const int j = j0 + r;
-        auto* lds = (__attribute__((address_space(3))) void*)(base + (isv ? BN * D : 0) + 64 * 8 * ins);
+        auto* lds = (__attribute__((address_space(3))) void*)(base + (isv ? BN * KW : 0) + 64 * 8 * ins);
         if (prev_rows == 0) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, lds, 16, j * rb + c16, 0, 0, 0);
         } else if (j >= prev_rows) {
@@ -71,22 +73,30 @@ __device__ __forceinline__ void state_load_tile(lds_u16* base, int wave, int lan
     }
 }
 
+// Waves per workgroup for head dim D and feature map PHI (the tile loads must
+// split evenly over them).
+constexpr int state_nw(int d, int phi) {
+    return phi == kPhiFeat && d == 32 ? 4 : state_waves(phi == kPhiElu1 ? d : 2 * d);
+}
+
 template <int D, int PHI>
-__global__ __launch_bounds__(state_waves(PHI == kPhiPoly2 ? 2 * D : D) * 64) void state_bf16_kernel(StateParams p) {
-    constexpr int DP = PHI == kPhiPoly2 ? 2 * D : D;
-    constexpr int NW = state_waves(DP), BN = kStateBN, NS = kStateStages;
+__global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(StateParams p) {
+    constexpr bool FEAT = PHI == kPhiFeat;            // phi(k) rows come precomputed
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
+    constexpr int KW = FEAT ? DP : D;                 // columns of the K tile
+    constexpr int NW = state_nw(D, PHI), BN = kStateBN, NS = FEAT ? 3 : kStateStages;
     constexpr int NT = DP / 32;                       // 32-wide feature tiles
     constexpr int NTW = NT >= NW ? NT / NW : 1;       // feature tiles per wave
     constexpr int SPLIT = NT >= NW ? 1 : NW / NT;     // waves sharing a feature tile
     constexpr int DT = D / 32;
     constexpr int C = D / 8;
-    constexpr int TILE = BN * D;                      // elements of one K (or V) tile
-    constexpr int STAGE = 2 * TILE;
-    constexpr int NINST = BN * C / 64;                // 1 KB load instructions per K (or V) tile
-    constexpr int OPW = 2 * NINST / NW;               // per wave and stage
+    constexpr int KTILE = BN * KW;                    // elements of the K tile
+    constexpr int STAGE = KTILE + BN * D;             // K tile, then the V tile
+    constexpr int NLD = STAGE * 2 / 1024;             // 1 KB load instructions per stage
+    constexpr int OPW = NLD / NW;                     // per wave and stage
     constexpr int KSTEPS = BN / 16;
     static_assert(NT % NW == 0 || NW % NT == 0, "feature tiles must split evenly over the waves");
-    static_assert(2 * NINST % NW == 0, "tile loads must split evenly over the waves");
+    static_assert(NLD % NW == 0, "tile loads must split evenly over the waves");
     static_assert(KSTEPS % SPLIT == 0, "16-key steps must split evenly over the waves sharing a tile");
     static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
 
@@ -126,20 +136,21 @@ __global__ __launch_bounds__(state_waves(PHI == kPhiPoly2 ? 2 * D : D) * 64) voi
     float* outp = p.partial + ((long long)(bh * p.n_blocks + u) * p.n_sub + sub) * (D * DP + DP);
 
     // resources end at the block's last row: rows past it read as zero
-    const int rb = D * 2;
+    const int rb = D * 2, krb = KW * 2;
     const int prev_rows = p.prev_rows;
-    const uint16_t* kb = (const uint16_t*)p.k + bh * p.bh_stride;
+    const uint16_t* kb = FEAT ? (const uint16_t*)p.fk + bh * p.fk_bh_stride : (const uint16_t*)p.k + bh * p.bh_stride;
     const uint16_t* vb = (const uint16_t*)p.v + bh * p.bh_stride;
-    const uint16_t* kpb = p.kp ? (const uint16_t*)p.kp + bh * p.prev_bh_stride : kb;
+    const void* kp = FEAT ? p.fkp : p.kp;
+    const uint16_t* kpb = kp ? (const uint16_t*)kp + bh * (FEAT ? p.fkp_bh_stride : p.prev_bh_stride) : kb;
     const uint16_t* vpb = p.vp ? (const uint16_t*)p.vp + bh * p.prev_bh_stride : vb;
     const int clip_rows = max(e1 - prev_rows, 0);
     const int prev_end = min(e1, prev_rows);
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, clip_rows * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, clip_rows * krb, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, clip_rows * rb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc((void*)kpb, (short)0, prev_end * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc((void*)kpb, (short)0, prev_end * krb, 0x00020000);
     const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc((void*)vpb, (short)0, prev_end * rb, 0x00020000);
     auto load_tile = [&](lds_u16* base, int t) {
-        state_load_tile<D, BN, NW, OPW, NINST>(base, wave, lane, j0 + t * BN, prev_rows, krs, vrs, kprs, vprs);
+        state_load_tile<D, KW, BN, NW, OPW>(base, wave, lane, j0 + t * BN, prev_rows, krs, vrs, kprs, vprs);
     };
 
     // transposing-read addressing (see lds_read_tr): for its column, lane
@@ -155,6 +166,16 @@ __global__ __launch_bounds__(state_waves(PHI == kPhiPoly2 ? 2 * D : D) * 64) voi
         const int ch = 4 * c + tr_chunk;
         toff[c][0] = tr_row * D + ((ch ^ swz<C>(tr_row)) << 3) + tr_sub;
         toff[c][1] = (tr_row + 8) * D + ((ch ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
+    }
+    // the same for the KW-wide feature tile (precomputed phi(k) rows)
+    int foff[FEAT ? NTW : 1][2];
+    if constexpr (FEAT) {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int ch = 4 * (nt0 + i * NW) + tr_chunk;
+            foff[i][0] = tr_row * KW + ((ch ^ swz<KW / 8>(tr_row)) << 3) + tr_sub;
+            foff[i][1] = (tr_row + 8) * KW + ((ch ^ swz<KW / 8>(tr_row + 8)) << 3) + tr_sub;
+        }
     }
 
     f32x16 acc[NTW][DT];
@@ -179,6 +200,30 @@ __global__ __launch_bounds__(state_waves(PHI == kPhiPoly2 ? 2 * D : D) * 64) voi
             for (int dt = 0; dt < DT; ++dt)
                 a[dt] = cat(lds_read_tr(Vs, r16 + toff[dt][0]), lds_read_tr(Vs, r16 + toff[dt][1]));
             const int kbase = t * BN + 16 * ks + 4 * h;  // key of element 0 (elements 4..7: +8)
+            if constexpr (FEAT) {
+                // phi(k) is already bf16: one MFMA per output tile, no split
+#pragma unroll
+                for (int i = 0; i < NTW; ++i) {
+                    bf16x8 b = cat(lds_read_tr(Ks, 16 * ks * KW + foff[i][0]), lds_read_tr(Ks, 16 * ks * KW + foff[i][1]));
+                    if (TAIL) {
+                        u32x4 w = __builtin_bit_cast(u32x4, b);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = kbase + (e < 2 ? 2 * e : 2 * e + 4);  // elements 2e, 2e+1
+                            const uint32_t lo = key < nkeys ? 0xffffu : 0u, hi = key + 1 < nkeys ? 0xffff0000u : 0u;
+                            w[e] &= lo | hi;
+                        }
+                        b = __builtin_bit_cast(bf16x8, w);
+                    }
+                    float f[8];
+                    unpack8(__builtin_bit_cast(u32x4, b), f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) zpart[i] += f[e];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) acc[i][dt] = mfma32x32x16(a[dt], b, acc[i][dt]);
+                }
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
                 const int nt = nt0 + i * NW;
@@ -215,8 +260,8 @@ __global__ __launch_bounds__(state_waves(PHI == kPhiPoly2 ? 2 * D : D) * 64) voi
     // pointers they keep the transposing reads clear of a wait for the loads
     auto iteration = [&](int t, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
         if (t + NS - 1 < ntiles) load_tile(fill, t + NS - 1);
-        if ((t + 1) * BN <= nkeys) tile_steps(std::false_type{}, t, cur, cur + TILE);
-        else tile_steps(std::true_type{}, t, cur, cur + TILE);
+        if ((t + 1) * BN <= nkeys) tile_steps(std::false_type{}, t, cur, cur + KTILE);
+        else tile_steps(std::true_type{}, t, cur, cur + KTILE);
     };
 
     for (int t = 0; t < NS - 1 && t < ntiles; ++t) load_tile(smem + t * STAGE, t);
@@ -278,8 +323,9 @@ hipError_t launch_d(const StateParams& p, hipStream_t s) {
     const long long blocks = (long long)p.BH * p.n_blocks * p.n_sub;
     if (blocks <= 0) return hipSuccess;
     switch (p.phi) {
-    case kPhiElu1: state_bf16_kernel<D, kPhiElu1><<<(unsigned)blocks, state_waves(D) * 64, 0, s>>>(p); break;
-    case kPhiPoly2: state_bf16_kernel<D, kPhiPoly2><<<(unsigned)blocks, state_waves(2 * D) * 64, 0, s>>>(p); break;
+    case kPhiElu1: state_bf16_kernel<D, kPhiElu1><<<(unsigned)blocks, state_nw(D, kPhiElu1) * 64, 0, s>>>(p); break;
+    case kPhiPoly2: state_bf16_kernel<D, kPhiPoly2><<<(unsigned)blocks, state_nw(D, kPhiPoly2) * 64, 0, s>>>(p); break;
+    case kPhiFeat: state_bf16_kernel<D, kPhiFeat><<<(unsigned)blocks, state_nw(D, kPhiFeat) * 64, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -106,3 +106,22 @@ def custom(B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frame
     return Workload(f"custom_{B}x{H}x{frames}x{tokens_per_frame}x{head_dim}", seed_id, B, H,
                     head_dim, frames, tokens_per_frame, chunk_frames, overlap_frames, dtype,
                     key_scale)
+
+
+def make_mlp_weights(seed_id: int, side: int, H: int, head_dim: int, hidden: int, dtype: str = "bf16",
+                     input_scale: float = 1.0):
+    """Seeded synthetic weights of one learned feature map (side 0: queries, 1:
+    keys); there are no trained weights to load.  Returns float32 torch tensors
+    (w1 [H, hidden, d] and w2 [H, 2d, hidden] rounded to the workload dtype and
+    back, b1 [H, hidden], b2 [H, 2d]).  Scales keep the activations O(1):
+    W1 ~ N(0, 1/(d s^2)) for inputs of rms s, b1 ~ N(0, 0.5^2), W2 ~ N(0,
+    1/hidden), b2 ~ N(0, 0.1^2); seeds default_rng(1000*seed_id + 10 + 4*side + i)."""
+    base = 1000 * seed_id + 10 + 4 * side
+    w1 = _draw(base + 0, (H, hidden, head_dim), 1.0 / (math.sqrt(head_dim) * input_scale))
+    b1 = _draw(base + 1, (H, hidden), 0.5)
+    w2 = _draw(base + 2, (H, 2 * head_dim, hidden), 1.0 / math.sqrt(hidden))
+    b2 = _draw(base + 3, (H, 2 * head_dim), 0.1)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    w1t = torch.from_numpy(w1).to(tdt).to(torch.float32)
+    w2t = torch.from_numpy(w2).to(tdt).to(torch.float32)
+    return w1t, torch.from_numpy(b1), w2t, torch.from_numpy(b2)
