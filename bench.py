@@ -12,8 +12,9 @@ against the bf16 MFMA roofline (its duration taken from HIP events recorded
 around that kernel on its own stream during the timed steps), the state pass
 against the HBM roofline, the dense bidirectional softmax companion at the same
 shape, the bidirectional hybrid form (§3.2 with overlap: later chunks join the
-linear set) at the same shape, and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+linear set) at the same shape, the same step with learned two-layer-MLP
+feature maps (seeded synthetic weights), and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -37,8 +38,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "2c23fbfabad2682a", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (257694 * 2.0 + 101477 * 1.0) * 1024}
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "7b74d4fb196f320e", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (256445 * 2.0 + 101472 * 1.0) * 1024}
 
 
 LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h", "kernels.h")
@@ -147,6 +148,98 @@ def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=Tru
     return res
 
 
+def length_scaling_bench(rh, hip, inputs, warmup):
+    """Forward time against clip length: the first F = 21, 42, ..., 105 latent
+    frames (1560 tokens each) of the 105-frame workload, T_c = 3, T_o = 1,
+    elu+1; least-squares line, its R^2, and the 105 frames again as 35
+    streaming steps of 3 frames (the chunk-wise RNN form), with the device
+    memory high-water of the streaming loop at 21 and at 105 frames."""
+    import numpy as np
+    import torch
+    wl = inputs.WORKLOADS["wan_long_105x30x52"]
+    HW = wl.tokens_per_frame
+    q, k, v = (x.to("cuda") for x in inputs.make_qkv(wl))
+    frames = [21, 42, 63, 84, 105]
+    ms = []
+    for F in frames:
+        n = F * HW
+        qs, ks, vs = (x[:, :, :n].contiguous() for x in (q, k, v))
+        out = torch.empty_like(qs)
+        wF = wl.with_(frames=F)
+        t = time_steps(rh, hip, qs, ks, vs, out, wF, 3, 1, "elu1", 5, warmup, profile=False)
+        ms.append(t["ms_per_step"])
+        del qs, ks, vs, out
+    x, y = np.array(frames, float), np.array(ms)
+    a, b = np.polyfit(x, y, 1)
+    r2 = 1.0 - float(((y - (a * x + b)) ** 2).sum() / ((y - y.mean()) ** 2).sum())
+
+    def stream(F):
+        st = rh.StepState(1, wl.H, HW, wl.head_dim, 3, 1, "elu1")
+        chunks = [tuple(x[:, :, 3 * i * HW:3 * (i + 1) * HW].contiguous() for x in (q, k, v))
+                  for i in range(F // 3)]
+        outs = [torch.empty_like(c[0]) for c in chunks]
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        t0 = time.perf_counter()
+        for c, o in zip(chunks, outs):
+            st.step(*c, out=o)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        return dt, torch.cuda.max_memory_allocated() - base, st.nbytes
+
+    stream(21)  # warm-up
+    dt105, hw105, sb105 = stream(105)
+    _, hw21, sb21 = stream(21)
+    return {"frames": frames, "ms_per_fwd": [round(m, 4) for m in ms],
+            "slope_ms_per_21_frames": round(a * 21, 4), "intercept_ms": round(b, 4), "r2": round(r2, 5),
+            "stream_105_frames": {"steps": 35, "ms": round(dt105 * 1000.0, 3),
+                                  "tokens_per_s": round(105 * HW / dt105, 1),
+                                  "state_bytes": sb105, "state_bytes_at_21_frames": sb21,
+                                  "extra_device_bytes_105": hw105, "extra_device_bytes_21": hw21}}
+
+
+def learned_map_bench(rh, hip, inputs, q, k, v, out, w, Tc, To, hidden, steps, cnt):
+    """The same step with the learned feature maps (seeded synthetic weights,
+    two-layer MLP of `hidden` units per head and side, D' = 2d), and the
+    feature-map kernel alone over every query row of the clip against the bf16
+    MFMA roofline (2 (hidden d + 2d hidden) flops per row)."""
+    import torch
+    maps = []
+    for side, scale in ((0, 1.0), (1, w.key_scale)):
+        w1, b1, w2, b2 = inputs.make_mlp_weights(w.seed_id, side, w.H, w.head_dim, hidden, w.dtype, scale)
+        maps.append(rh.MlpWeights(w1.to(torch.bfloat16).cuda(), b1.cuda(), w2.to(torch.bfloat16).cuda(),
+                                  b2.cuda()))
+    pair = tuple(maps)
+    t = time_steps(rh, hip, q, k, v, out, w, Tc, To, pair, steps, 1)
+    d = w.head_dim
+    phi_out = torch.empty(w.B, w.H, w.N, 2 * d, dtype=q.dtype, device=q.device)
+    for _ in range(2):
+        rh.feature_mlp(q, pair[0], out=phi_out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        rh.feature_mlp(q, pair[0], out=phi_out)
+    e1.record()
+    torch.cuda.synchronize()
+    mlp_ms = e0.elapsed_time(e1) / reps
+    rows = w.B * w.H * w.N
+    flops = 2.0 * rows * (hidden * d + 2 * d * hidden)
+    tflops = flops / (mlp_ms / 1000.0) / 1e12
+    return {"tokens_per_s": round(w.tokens / (t["ms_per_step"] / 1000.0), 1),
+            "ms_per_step": round(t["ms_per_step"], 4), "hidden": hidden, "feature_dim": 2 * d,
+            "map_and_state_ms": round(t["state_ms"], 4), "scan_ms": round(t["scan_ms"], 4),
+            "local_ms": round(t["local_ms"], 4),
+            "local_tflops": round(cnt["softmax_flops"] / (t["local_ms"] / 1000.0) / 1e12, 2),
+            "feature_kernel": {"kernel": "phi_mlp_bf16_kernel", "rows": rows, "ms": round(mlp_ms, 4),
+                               "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                               "algorithmic_flops": flops,
+                               "hbm_gbs": round(rows * d * 2 * 3 / (mlp_ms / 1000.0) / 1e9, 1)}}
+
+
 def cpu_baseline(w, q, k, v, Tc, To, phi, target_s=15.0):
     """fp64 oracle (definition form) on a bounded, chunk-stratified sample of query rows."""
     import numpy as np
@@ -186,6 +279,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-bidir", action="store_true")
+    ap.add_argument("--no-learned", action="store_true")
+    ap.add_argument("--no-length", action="store_true")
+    ap.add_argument("--learned-hidden", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -266,6 +362,15 @@ def main():
                                                / PEAK_HBM_GBS, 4),
                          state_algorithmic_bytes=cnt["bidir_state_bytes"])
 
+    learned = None
+    if not args.no_learned:
+        learned = learned_map_bench(rh, hip, inputs, qg, kg, vg, out, w, Tc, To, args.learned_hidden,
+                                    max(3, args.steps // 2), cnt)
+
+    length = None
+    if not args.no_length and w.name == "wan_21x30x52" and Tc == 3 and phi == "elu1":
+        length = length_scaling_bench(rh, hip, inputs, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, Tc, To, phi, args.cpu_seconds)
@@ -284,6 +389,8 @@ def main():
         "state_pass": state,
         "dense_softmax": dense,
         "bidirectional": bidir,
+        "learned_map": learned,
+        "length_scaling": length,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -287,12 +287,16 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     // being read are passed as restrict pointers: they never overlap, and the
     // compiler may then keep the transposing V reads clear of the wait for the
     // loads still in flight (it cannot otherwise tell them apart).
-    // the linear branch's prepared state S_t^T (elu+1: [D][D], hi and lo parts)
-    // is staged in LDS by the last iteration, into the slot no tile needs any
-    // more, so the epilogue reads it from there instead of every wave loading
-    // it from L2
+    // the linear branch's prepared state S_t^T ([D][D'], hi and lo parts) is
+    // staged in LDS so that the epilogue reads it from there instead of every
+    // wave loading it from L2: both parts by the last iteration into the slot
+    // no tile needs any more when they fit in one slot, else the hi part then
+    // and the lo part into the last tile's slot once every wave is done with it
     const bool lin = PHI != kPhiNone && (p.lin_always || w0 > 0);
-    constexpr bool STAGE_S = PHI == kPhiElu1 && 2 * D * D <= STAGE;
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
+    constexpr int SPART = D * DP;                       // elements of one part
+    constexpr bool STAGE_S = PHI != kPhiNone && SPART <= STAGE;
+    constexpr bool S_ONE_SLOT = 2 * SPART <= STAGE;
     const uint16_t* shi = nullptr;
     const uint16_t* slo = nullptr;
     if (STAGE_S && lin) {
@@ -303,8 +307,10 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         if (it + PF < ntiles)
             issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(fill, wave, it + PF, p.prev_rows, seg_shift, rb, op_row,
                                                            op_c16, krs, vrs, kprs, vprs);
-        else if (STAGE_S && lin && it == ntiles - 1)
-            issue_state_dma<D, D, NW>(fill, wave, lane, shi, slo);
+        else if (STAGE_S && lin && it == ntiles - 1) {
+            issue_state_dma<D, DP, NW>(fill, wave, lane, shi);
+            if (S_ONE_SLOT) issue_state_dma<D, DP, NW>(fill + SPART, wave, lane, slo);
+        }
         scores_softmax(it, cur);
         pv(cur + KTILE);
     };
@@ -322,15 +328,27 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
 
     // ---------------------------------------------------------------- epilogue
     const lds_u16* s_lds = nullptr;
+    const lds_u16* s_lds_lo = nullptr;
     if (STAGE_S && lin) {
+        lds_u16* hi_slot = smem + ((ntiles - 1 + PF) % STAGES) * STAGE;
+        if constexpr (S_ONE_SLOT) {
+            s_lds_lo = hi_slot + SPART;
+        } else {
+            // every wave is done reading the last tile: its slot takes the lo part
+            lds_u16* lo_slot = smem + ((ntiles - 1) % STAGES) * STAGE;
+            lds_barrier();
+            issue_state_dma<D, DP, NW>(lo_slot, wave, lane, slo);
+            s_lds_lo = lo_slot;
+        }
         __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // own share of the staged state
         lds_barrier();                               // everyone's
-        s_lds = smem + ((ntiles - 1 + PF) % STAGES) * STAGE;
+        s_lds = hi_slot;
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
         finish_query_block<D, PHI>(p, qreg[qb], oacc[qb], msum[qb], m2[qb], mtrue[qb],
-                                   q_start + (wave * QB + qb) * 32 + lq, q_end, bh, t, h, lq, lin, s_lds);
+                                   q_start + (wave * QB + qb) * 32 + lq, q_end, bh, t, h, lq, lin, s_lds,
+                                   s_lds_lo);
 }
 
 // Tile configuration: QB query blocks of 32 per wave, NW waves, BN keys per LDS

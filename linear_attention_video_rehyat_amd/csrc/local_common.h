@@ -38,17 +38,15 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Global->LDS copy of the prepared state S_t^T (bf16 hi part at dst, lo part
-// right after it, each [D][DP] row-major with the 16-byte chunks of row r
-// XOR-swizzled by swz(r)), spread over the NW waves of a workgroup.
+// Global->LDS copy of one part (bf16 hi or lo) of the prepared state S_t^T,
+// [D][DP] row-major with the 16-byte chunks of row r XOR-swizzled by swz(r),
+// spread over the NW waves of a workgroup.
 template <int D, int DP, int NW>
-__device__ __forceinline__ void issue_state_dma(lds_u16* dst, int wave, int lane, const uint16_t* shi,
-                                                const uint16_t* slo) {
+__device__ __forceinline__ void issue_state_dma(lds_u16* dst, int wave, int lane, const uint16_t* src) {
     constexpr int CS = DP / 8;                   // 16-byte chunks per row
     constexpr int NI = D * DP * 2 / 1024;        // 1 KB instructions per matrix
     constexpr int PER = (NI + NW - 1) / NW;
-    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc((void*)shi, (short)0, D * DP * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)slo, (short)0, D * DP * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, D * DP * 2, 0x00020000);
 #pragma unroll
     for (int o = 0; o < PER; ++o) {
         const int ins = wave + o * NW;
@@ -56,10 +54,8 @@ __device__ __forceinline__ void issue_state_dma(lds_u16* dst, int wave, int lane
             const int pos = 64 * ins + lane;
             const int r = pos / CS;
             const int off = r * DP * 2 + ((pos % CS) ^ swz<CS>(r)) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, (__attribute__((address_space(3))) void*)(dst + 512 * ins),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * ins),
                                                      16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                lrs, (__attribute__((address_space(3))) void*)(dst + D * DP + 512 * ins), 16, off, 0, 0, 0);
         }
     }
 }
@@ -78,7 +74,8 @@ template <int D, int PHI>
 __device__ __forceinline__ void finish_query_block(const LocalParams& p, const bf16x8 (&q)[D / 16],
                                                    const f32x16 (&oacc)[D / 32], float msum, float m2,
                                                    float mtrue, int row, int q_end, int bh, int t, int h,
-                                                   int lq, bool lin, const lds_u16* s_lds = nullptr) {
+                                                   int lq, bool lin, const lds_u16* s_lds = nullptr,
+                                                   const lds_u16* s_lds_lo = nullptr) {
     constexpr int KS = D / 16, DT = D / 32;
     constexpr bool FEAT = PHI == kPhiFeat;  // phi(q) precomputed in bf16: no lo part
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
@@ -86,8 +83,9 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
     const float lsum = xhalf_sum(msum);
     lin = PHI != kPhiNone && lin;
     // phi(q): n^L in fp32 and the bf16 hi/lo MFMA operands, kept in registers
-    // unless there are too many of them (then formed again per output slice)
-    constexpr bool KEEP = KSL <= 8;
+    // unless there are too many of them (then formed again per output slice);
+    // a precomputed phi(q) has no lo part and is always kept
+    constexpr bool KEEP = FEAT || KSL <= 8;
     const uint16_t* fqrow =
         FEAT ? (const uint16_t*)p.fq + bh * p.fq_bh_stride + (long long)min(row, q_end - 1) * DP + 8 * h : nullptr;
     auto phi_frag = [&](int ksl, bf16x8& fh, bf16x8& fl, float* f) {
@@ -112,7 +110,7 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
         fh = __builtin_bit_cast(bf16x8, whi);
         fl = __builtin_bit_cast(bf16x8, wlo);
     };
-    bf16x8 fhi[KEEP ? KSL : 1], flo[KEEP ? KSL : 1];
+    bf16x8 fhi[KEEP ? KSL : 1], flo[KEEP && !FEAT ? KSL : 1];
     float nl = 0.0f;
     const uint16_t* shi = nullptr;
     const uint16_t* slo = nullptr;
@@ -128,7 +126,7 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
             phi_frag(ksl, fh, fl, f);
             if (KEEP) {
                 fhi[KEEP ? ksl : 0] = fh;
-                flo[KEEP ? ksl : 0] = fl;
+                if (!FEAT) flo[KEEP && !FEAT ? ksl : 0] = fl;
             }
             const f32x4 z0 = *(const f32x4*)(zp + 16 * ksl + 8 * h);
             const f32x4 z1 = *(const f32x4*)(zp + 16 * ksl + 8 * h + 4);
@@ -165,10 +163,10 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
 #pragma unroll
             for (int ksl = 0; ksl < KSL; ++ksl) {
                 bf16x8 ahi, alo;
-                if (s_lds) {  // copy staged in LDS by issue_state_dma (DP / 8 chunks per row)
+                if (s_lds) {  // copies staged in LDS by issue_state_dma (DP / 8 chunks per row)
                     const int off = (32 * dt + lq) * DP + (((2 * ksl + h) ^ swz<DP / 8>(lq)) << 3);
                     ahi = lds_read_b128(s_lds, off);
-                    alo = lds_read_b128(s_lds, D * DP + off);
+                    alo = lds_read_b128(s_lds_lo, off);
                 } else {
                     const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
                     ahi = __builtin_bit_cast(bf16x8, ldg_b128(shi + off));
@@ -177,7 +175,7 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
                 bf16x8 fh, fl;
                 if (KEEP) {
                     fh = fhi[KEEP ? ksl : 0];
-                    fl = flo[KEEP ? ksl : 0];
+                    fl = FEAT ? bf16x8{} : flo[KEEP && !FEAT ? ksl : 0];
                 } else {
                     float f[8];
                     phi_frag(ksl, fh, fl, f);

@@ -19,6 +19,9 @@
 // to the B fragment in registers, in fp32, and split into bf16 hi + lo parts,
 // so the products carry ~16 significant bits of phi(k) while v is exact in
 // bf16.  z is summed on the vector ALU from the unsplit fp32 values.
+// With the learned feature maps (kPhiFeat) phi(k) comes precomputed in bf16:
+// the K tile holds phi(k) rows (D' = 2 head_dim columns, a 3-stage ring), its
+// transposing reads are the B fragments as they are, one MFMA per output tile.
 #include <type_traits>
 
 #include "local_common.h"
