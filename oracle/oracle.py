@@ -318,3 +318,48 @@ def recurrent(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, p
         out[:, :, sl] = st.step(q[:, :, sl], k[:, :, sl], v[:, :, sl])
         sizes.append(st.S.nbytes + st.z.nbytes + st.k_prev.nbytes + st.v_prev.nbytes)
     return (out, sizes, st) if return_state_sizes else out
+
+
+# ---------------------------------------------------------------------------
+# gradients (the training direction: distillation and fine-tuning, ReHyAt §3.4)
+# ---------------------------------------------------------------------------
+
+def _torch_feature(x, phi, side):
+    """phi of §3.1/§3.2 on torch fp64 tensors (differentiable)."""
+    import torch
+    kind = phi_kind(phi)
+    if kind == PHI_GIVEN:
+        m = phi[side]
+        h = torch.relu(torch.einsum("bhnd,hkd->bhnk", x, torch.from_numpy(m.w1))
+                       + torch.from_numpy(m.b1)[None, :, None, :])
+        psi = torch.einsum("bhnk,hmk->bhnm", h, torch.from_numpy(m.w2)) + torch.from_numpy(m.b2)[None, :, None, :]
+        half = psi.shape[-1] // 2
+        p1, p2 = psi[..., :half], psi[..., half:]
+        return torch.cat([torch.where(p1 > 0, p1 + 1.0, torch.exp(torch.clamp(p1, max=0.0))), p2 * p2], dim=-1)
+    e = torch.where(x > 0, x + 1.0, torch.exp(torch.clamp(x, max=0.0)))
+    if kind == PHI_ELU1:
+        return e
+    if kind == PHI_POLY2:
+        return torch.cat([e, x * x], dim=-1)
+    raise ValueError(phi)
+
+
+def backward(q, k, v, dy, tokens_per_frame, chunk_frames, overlap_frames, phi="elu1", scale=1.0,
+             causal=True):
+    """(dq, dk, dv) = gradients of sum(dy * y) for the hybrid output y, by
+    reverse-mode differentiation (torch autograd, fp64, CPU) of the matrix form
+    of :func:`brute_force`: W = exp(s QK^T) M_S + (phi(Q) phi(K)^T) M_L,
+    Y = W V / rowsum(W).  Tiny and mid-size inputs (it builds N x N matrices)."""
+    import torch
+    Q, K, V = (torch.tensor(_f64(x), requires_grad=True) for x in (q, k, v))
+    G = torch.tensor(_f64(dy))
+    N = Q.shape[-2]
+    m_s, m_l = (torch.from_numpy(m) for m in masks(N, tokens_per_frame, chunk_frames, overlap_frames, causal))
+    s = scale * (Q @ K.transpose(-1, -2))
+    w = torch.where(m_s, torch.exp(torch.where(m_s, s, torch.zeros_like(s))), torch.zeros_like(s))
+    if phi_kind(phi) != PHI_NONE:
+        lin = _torch_feature(Q, phi, 0) @ _torch_feature(K, phi, 1).transpose(-1, -2)
+        w = w + torch.where(m_l, lin, torch.zeros_like(lin))
+    y = (w @ V) / w.sum(dim=-1, keepdim=True)
+    y.backward(G)
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()

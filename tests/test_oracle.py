@@ -370,3 +370,55 @@ def test_mlp_map_random_weights_small_loops():
             want = [p + 1.0 if p > 0 else math.exp(p) for p in psi[:m2 // 2]] + [p * p for p in psi[m2 // 2:]]
             np.testing.assert_allclose(got[0, h, n], want, rtol=1e-13)
     assert (got >= 0).all()
+
+
+# ------------------------------------------------------------------ gradients
+
+@pytest.mark.parametrize("phi", ["elu1", "poly2", "none"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_gradients_match_finite_differences(phi, causal):
+    """Central differences of the C definition form (an implementation that
+    shares nothing with the autograd matrix form) on every input coordinate of a
+    tiny case."""
+    rng = np.random.default_rng(21)
+    B, H, F, HW, d, Tc, To = 1, 1, 4, 2, 3, 1, 1
+    q, k, v = rand_qkv(rng, B, H, F * HW, d, kscale=0.7)
+    dy = rng.standard_normal(q.shape)
+    dq, dk, dv = O.backward(q, k, v, dy, HW, Tc, To, phi, causal=causal)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if a is x else a for a in (q, k, v)]
+            args_m = [xm if a is x else a for a in (q, k, v)]
+            yp = O.definition(*args_p, F, HW, Tc, To, phi, causal=causal)
+            ym = O.definition(*args_m, F, HW, Tc, To, phi, causal=causal)
+            num[idx] = ((yp - ym) * dy).sum() / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_gradients_single_chunk_are_softmax_attention_gradients():
+    """T_c >= F: the hybrid is softmax attention; its gradients are those of
+    torch's scaled_dot_product_attention (fp64)."""
+    rng = np.random.default_rng(22)
+    q, k, v = rand_qkv(rng, 1, 2, 24, 8, kscale=0.5)
+    dy = rng.standard_normal(q.shape)
+    dq, dk, dv = O.backward(q, k, v, dy, 6, 4, 1, "elu1")
+    t = [torch.tensor(x, requires_grad=True) for x in (q, k, v)]
+    y = torch.nn.functional.scaled_dot_product_attention(*t, scale=1.0)
+    y.backward(torch.from_numpy(dy))
+    for a, b in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(a, b.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_gradient_of_v_sums_to_gradient_of_y():
+    """Each output is a convex combination of values, so sum_j dv_j = sum_i dy_i."""
+    rng = np.random.default_rng(23)
+    q, k, v = rand_qkv(rng, 2, 1, 30, 4, kscale=0.5)
+    dy = rng.standard_normal(q.shape)
+    for phi in ("elu1", "poly2"):
+        _, _, dv = O.backward(q, k, v, dy, 5, 2, 1, phi)
+        np.testing.assert_allclose(dv.sum(axis=-2), dy.sum(axis=-2), rtol=1e-12, atol=1e-12)
