@@ -15,8 +15,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["RehyatError", "attn_fwd", "attn_fwd_partials", "StepState", "feature_map_id",
-           "MlpWeights", "feature_mlp", "library_path", "load_library", "exported_symbols"]
+__all__ = ["RehyatError", "attn_fwd", "attn_fwd_partials", "attn_fwd_lse", "attn_bwd", "StepState",
+           "feature_map_id", "MlpWeights", "feature_mlp", "library_path", "load_library", "exported_symbols"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "librehyat.so")
@@ -31,6 +31,7 @@ exported_symbols = (
     "rehyat_attn_fwd_bidir", "rehyat_attn_fwd_bidir_f32", "rehyat_attn_fwd_bidir_partials",
     "rehyat_step_state_bytes", "rehyat_step_state_init", "rehyat_attn_step",
     "rehyat_feature_mlp", "rehyat_attn_fwd_mlp", "rehyat_attn_fwd_mlp_partials", "rehyat_attn_step_mlp",
+    "rehyat_attn_fwd_lse", "rehyat_attn_bwd",
     "rehyat_set_profile_events", "rehyat_status_string", "rehyat_last_error", "rehyat_version",
 )
 
@@ -93,6 +94,10 @@ def load_library():
     lib.rehyat_attn_fwd_mlp_partials.restype = i
     lib.rehyat_attn_step_mlp.argtypes = [ctypes.POINTER(_StepStateC), vp, vp, vp, vp, i, mp, mp, vp]
     lib.rehyat_attn_step_mlp.restype = i
+    lib.rehyat_attn_fwd_lse.argtypes = [vp] * 5 + [i] * 9 + [vp]
+    lib.rehyat_attn_fwd_lse.restype = i
+    lib.rehyat_attn_bwd.argtypes = [vp] * 9 + [i] * 9 + [vp]
+    lib.rehyat_attn_bwd.restype = i
     lib.rehyat_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     lib.rehyat_set_profile_events.restype = i
     lib.rehyat_status_string.argtypes = [i]
@@ -259,6 +264,45 @@ def attn_fwd_partials(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_f
     fn = lib.rehyat_attn_fwd_partials if causal else lib.rehyat_attn_fwd_bidir_partials
     _check(fn(*ptrs, feature_map_id(feature_map), _stream_handle(stream)))
     return parts
+
+
+def attn_fwd_lse(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, feature_map="elu1",
+                 out=None, lse=None, stream=None):
+    """Forward (recurrent partition) that also returns lse [B, H, N] fp32 =
+    ln(n^S + n^L) per query, the normaliser the backward needs: (out, lse)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    _check(lib.rehyat_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   _dtype_id(q), B, H, frames, tokens_per_frame, d, chunk_frames,
+                                   overlap_frames, feature_map_id(feature_map), _stream_handle(stream)))
+    return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, frames, tokens_per_frame, chunk_frames, overlap_frames,
+             feature_map="elu1", grads=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for the recurrent hybrid
+    attention, given the forward's inputs, out and lse (attn_fwd_lse)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise RehyatError(1, f"{name} must match q")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise RehyatError(1, "lse must be a contiguous float32 [B, H, N] tensor")
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    _check(lib.rehyat_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _dtype_id(q),
+                               B, H, frames, tokens_per_frame, d, chunk_frames, overlap_frames,
+                               feature_map_id(feature_map), _stream_handle(stream)))
+    return dq, dk, dv
 
 
 def set_profile_events(events):

@@ -297,7 +297,8 @@ void mlp_rows(const Geometry& g, int mode, int& q0, int& k1) {
 
 rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g, int mode,
                       float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s,
-                      const rehyat_mlp_weights* wq = nullptr, const rehyat_mlp_weights* wk = nullptr) {
+                      const rehyat_mlp_weights* wq = nullptr, const rehyat_mlp_weights* wk = nullptr,
+                      float* lse = nullptr) {
     const bool lin = any_linear(g, mode);
     char* ws = nullptr;
     FwdWorkspace w{};
@@ -371,6 +372,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         lp.phi = REHYAT_PHI_NONE;  // no chunk has a linear set
     }
     lp.pm = pm; lp.pnt = pnt; lp.poS = poS; lp.poL = poL; lp.pnL = pnL;
+    lp.lse = lse;
     hipError_t e = g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s);
     if (e != hipSuccess) return hip_fail(e, "local-attention launch");
     if ((e = prof_mark(3, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -429,6 +431,127 @@ rehyat_status partials_entry(const void* q, const void* k, const void* v, int dt
         if (p && !aligned16(p)) return fail(REHYAT_EINVAL, "pointers must be 16-byte aligned");
     g_last_error.clear();
     return run_fwd(q, k, v, nullptr, g, mode, m, nt, o_s, o_l, n_l, (hipStream_t)stream, wq, wk);
+}
+
+// ---------------------------------------------------------------- backward
+// Workspace of the backward: dsum, the forward's prepared states (both
+// layouts), and the gradient sums per chunk-row block with their suffixes.
+struct BwdWorkspace {
+    size_t dsum_off, part_off, shi_off, slo_off, thi_off, tlo_off, z_off;
+    size_t gpart_off, ghi_off, glo_off, gthi_off, gtlo_off, gz_off, total;
+    int n_sub, gn_sub;
+    SubSplit split, gsplit;
+};
+
+BwdWorkspace bwd_workspace(const Geometry& g) {
+    BwdWorkspace w{};
+    const bool bf = g.dtype == REHYAT_BF16;
+    w.split = state_split(g.dtype, (long long)g.Tc * g.HW);   // delta blocks: at most T_c frames
+    w.gsplit = w.split;                                        // chunk-row blocks: at most T_c frames
+    w.n_sub = w.split.n_sub;
+    w.gn_sub = w.gsplit.n_sub;
+    const int U = std::max(g.C - 1, 0);
+    const size_t prep = (size_t)g.BH * g.C * g.d * g.Dp * (bf ? 2 : 4);
+    const size_t zs = (size_t)g.BH * g.C * g.Dp * 4;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+    w.dsum_off = take((size_t)g.BH * g.N * 4);
+    w.part_off = take((size_t)g.BH * U * w.n_sub * g.E * 4);
+    w.shi_off = take(prep);
+    w.slo_off = take(bf ? prep : 0);
+    w.thi_off = take(prep);
+    w.tlo_off = take(bf ? prep : 0);
+    w.z_off = take(zs);
+    w.gpart_off = take((size_t)g.BH * U * w.gn_sub * g.E * 4);
+    w.ghi_off = take(prep);
+    w.glo_off = take(bf ? prep : 0);
+    w.gthi_off = take(prep);
+    w.gtlo_off = take(bf ? prep : 0);
+    w.gz_off = take(zs);
+    w.total = off;
+    return w;
+}
+
+rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H, int frames,
+                        int tpf, int d, int Tc, int To, int phi, void* stream) {
+    Geometry g{};
+    rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
+    if (st != REHYAT_OK) return st;
+    const void* ins[6] = {q, k, v, out, lse, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (const void* x : ins)
+        if (!x || !aligned16(x)) return fail(REHYAT_EINVAL, "null or misaligned input pointer");
+    for (void* x : outs)
+        if (!x || !aligned16(x)) return fail(REHYAT_EINVAL, "null or misaligned gradient pointer");
+    const size_t bytes = (size_t)g.BH * g.N * g.d * g.elem;
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], bytes, ins[b], b == 4 ? (size_t)g.BH * g.N * 4 : bytes))
+                return fail(REHYAT_EINVAL, "gradients must not overlap the inputs");
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], bytes, outs[b], bytes)) return fail(REHYAT_EINVAL, "gradients must not overlap");
+    }
+    g_last_error.clear();
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = g.dtype == REHYAT_BF16;
+    const bool lin = any_linear(g, kCausal);
+    const BwdWorkspace w = bwd_workspace(g);
+    void* wsp = nullptr;
+    if ((st = arena_get(w.total, &wsp)) != REHYAT_OK) return st;
+    char* ws = (char*)wsp;
+
+    BwdParams bp{};
+    bp.q = q; bp.k = k; bp.v = v; bp.dy = dout; bp.out = out;
+    bp.lse = lse; bp.dsum = (const float*)(ws + w.dsum_off);
+    bp.dq = dq; bp.dk = dk; bp.dv = dv;
+    bp.bh_stride = g.N * g.d;
+    bp.N = (int)g.N; bp.HW = g.HW; bp.F = g.F; bp.Tc = g.Tc; bp.To = g.To; bp.C = g.C; bp.BH = g.BH;
+    bp.d = g.d; bp.phi = lin ? g.phi : REHYAT_PHI_NONE; bp.lin = lin ? 1 : 0;
+    hipError_t e = launch_bwd_dsum(bp, (float*)(ws + w.dsum_off), bf, s);
+    if (e != hipSuccess) return hip_fail(e, "backward dsum launch");
+    if (lin) {
+        const int U = g.C - 1;
+        // the forward's states S_t, z_t (both layouts of S_t)
+        StateParams sp{};
+        sp.k = k; sp.v = v; sp.bh_stride = g.N * g.d;
+        sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
+        sp.n_blocks = U; sp.sub_rows = w.split.sub_rows; sp.n_sub = w.n_sub;
+        sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi; sp.mode = kCausal; sp.F = g.F;
+        sp.partial = (float*)(ws + w.part_off);
+        e = bf ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
+        if (e != hipSuccess) return hip_fail(e, "block-state launch");
+        ScanParams cp{};
+        cp.partial = sp.partial;
+        cp.s_hi = ws + w.shi_off; cp.s_lo = ws + w.slo_off; cp.t_hi = ws + w.thi_off; cp.t_lo = ws + w.tlo_off;
+        cp.z = (float*)(ws + w.z_off);
+        cp.s_chunk_stride = (long long)g.d * g.Dp; cp.s_bh_stride = (long long)g.C * g.d * g.Dp;
+        cp.z_chunk_stride = g.Dp; cp.z_bh_stride = (long long)g.C * g.Dp;
+        cp.U = U; cp.n_sub = w.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
+        cp.t_first = 1; cp.t_offset = 0; cp.f32_prep = !bf; cp.mode = kCausal; cp.C = g.C;
+        if ((e = launch_scan(cp, s)) != hipSuccess) return hip_fail(e, "scan launch");
+        // gradient sums per chunk (rows: the chunk's queries, second operand dy)
+        StateParams gp = sp;
+        gp.k = q; gp.v = dout; gp.mode = kChunkRows;
+        gp.sub_rows = w.gsplit.sub_rows; gp.n_sub = w.gn_sub;
+        gp.row_lse = lse; gp.row_d = bp.dsum;
+        gp.partial = (float*)(ws + w.gpart_off);
+        e = bf ? launch_state_bf16(gp, s) : launch_state_f32(gp, s);
+        if (e != hipSuccess) return hip_fail(e, "gradient-state launch");
+        ScanParams gc = cp;
+        gc.partial = gp.partial; gc.n_sub = w.gn_sub;
+        gc.s_hi = ws + w.ghi_off; gc.s_lo = ws + w.glo_off; gc.t_hi = ws + w.gthi_off; gc.t_lo = ws + w.gtlo_off;
+        gc.z = (float*)(ws + w.gz_off);
+        gc.t_first = 0; gc.mode = kChunkRows;
+        if ((e = launch_scan(gc, s)) != hipSuccess) return hip_fail(e, "gradient scan launch");
+        bp.st_hi = ws + w.thi_off; bp.st_lo = ws + w.tlo_off; bp.z = (const float*)(ws + w.z_off);
+        bp.g_hi = ws + w.ghi_off; bp.g_lo = ws + w.glo_off;
+        bp.gt_hi = ws + w.gthi_off; bp.gt_lo = ws + w.gtlo_off; bp.gz = (const float*)(ws + w.gz_off);
+        bp.s_stride = (long long)g.d * g.Dp; bp.z_stride = g.Dp;
+    }
+    e = bf ? launch_bwd_bf16(bp, s) : launch_bwd_f32(bp, s);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return REHYAT_OK;
 }
 
 // ---------------------------------------------------------------- streaming state
@@ -707,6 +830,34 @@ rehyat_status rehyat_attn_fwd_mlp_partials(const void* q, const void* k, const v
     return partials_entry(q, k, v, dtype, m, nt, o_s, o_l, n_l, B, H, frames, tokens_per_frame, head_dim,
                           chunk_frames, overlap_frames, REHYAT_PHI_MLP2, causal ? kCausal : kBidirectional,
                           stream, phi_q, phi_k);
+}
+
+rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int dtype,
+                                  int B, int H, int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+                                  int overlap_frames, int feature_map, void* stream) {
+    Geometry g{};
+    rehyat_status st = check_common(g, B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
+                                    feature_map, dtype);
+    if (st != REHYAT_OK) return st;
+    if (!q || !k || !v || !out || !lse) return fail(REHYAT_EINVAL, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+        return fail(REHYAT_EINVAL, "tensor pointers must be 16-byte aligned");
+    const size_t bytes = (size_t)g.BH * g.N * g.d * g.elem, lbytes = (size_t)g.BH * g.N * 4;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes) ||
+        overlaps(lse, lbytes, out, bytes) || overlaps(lse, lbytes, q, bytes) || overlaps(lse, lbytes, k, bytes) ||
+        overlaps(lse, lbytes, v, bytes))
+        return fail(REHYAT_EINVAL, "out and lse must not overlap q, k, v or each other");
+    g_last_error.clear();
+    return run_fwd(q, k, v, out, g, kCausal, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream,
+                   nullptr, nullptr, lse);
+}
+
+rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H, int frames,
+                              int tokens_per_frame, int head_dim, int chunk_frames, int overlap_frames,
+                              int feature_map, void* stream) {
+    return bwd_entry(q, k, v, out, lse, dout, dq, dk, dv, dtype, B, H, frames, tokens_per_frame, head_dim,
+                     chunk_frames, overlap_frames, feature_map, stream);
 }
 
 rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int H, int rows, int head_dim,

@@ -1,0 +1,785 @@
+// bwd.hip -- backward of the ReHyAt hybrid attention (recurrent partition).
+//
+// Forward (arXiv 2601.04342, §3.1-§3.3): for query i of chunk t,
+//   y_i = (sum_{j in T^S_t} e^{q_i.k_j} v_j + sum_{j in T^L_t} (phi(q_i).phi(k_j)) v_j) / N_i,
+// N_i = n^S_i + n^L_i, lse_i = ln N_i.  With the weights w_ij (e^{q.k} on the
+// softmax set, phi(q).phi(k) on the linear set), D_i = dy_i . y_i and the
+// normalised weights w_ij / N_i:
+//   dv_j      = sum_i (w_ij / N_i) dy_i
+//   dw_ij     = (dy_i . v_j - D_i) / N_i
+//   softmax:  ds_ij = (w_ij / N_i)(dy_i . v_j - D_i);  dq_i += ds_ij k_j,  dk_j += ds_ij q_i
+//   linear:   dphi(q_i) = e^{-lse_i} (S_t dy_i - D_i z_t)          (S_t = sum_{T^L_t} phi(k) v^T)
+//             dphi(k_j) = G_u v_j - g_u,  dv_j += G_u^T phi(k_j)   (j in delta block E_u)
+//             G_u = sum_{t > u} sum_{i in chunk t} e^{-lse_i} phi(q_i) dy_i^T,
+//             g_u = sum_{t > u} sum_{i in chunk t} e^{-lse_i} D_i phi(q_i)
+//   dq_i += phi'(q_i) . dphi(q_i),  dk_j += phi'(k_j) . dphi(k_j)   (elementwise maps)
+// The G_u are the reverse-order (suffix) counterpart of the forward's state
+// scan; they come from the block-state kernel run over query rows with dy as
+// its second operand, and a suffix scan.
+//
+// bf16 kernels, both on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+//  * dk/dv: a workgroup of 4 waves owns 128 keys (32 per wave, their K and V
+//    fragments in registers) and streams the query rows of the chunks whose
+//    windows hold them (64-row Q and dY tiles in a 2-stage LDS ring, with each
+//    row's lse, D and window bounds).  Per 32 queries: S = Q K^T and dP = dY V^T
+//    (keys in the lane dimension), P and dS in registers, then dV^T += dY^T P
+//    and dK^T += Q^T dS with dY^T and Q^T read through the transposing LDS read
+//    in the key order of P's registers.  The linear branch of the wave's keys
+//    is added at the end from G_u (both layouts, bf16 hi/lo) and g_u.
+//  * dq: a workgroup of 4 waves owns 128 queries of one chunk (q and dy
+//    fragments in registers) and streams its window's K and V tiles (64 keys,
+//    2-stage ring).  Per 32 keys: S^T = K Q^T, dP^T = V dY^T, dS^T in registers,
+//    dQ^T += K^T dS^T (K^T by the transposing read).  The linear branch is added
+//    at the end from S_t (transposed layout, bf16 hi/lo) and z_t.
+// fp32 kernels: the same sums on the vector ALU (one query or key per lane).
+#include "local_common.h"
+
+namespace rehyat {
+
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per dk/dv workgroup
+constexpr int kBwdQRows = 64;              // query rows per dk/dv LDS tile
+constexpr int kBwdQueries = 32 * kBwdWaves;  // queries per dq workgroup
+constexpr int kBwdKTile = 64;              // keys per dq LDS tile
+
+// elu(x) + 1 and its derivative
+__device__ __forceinline__ float elu1_grad(float x) { return x > 0.0f ? 1.0f : __expf(x); }
+
+// dsum_i = dy_i . out_i: D/8 lanes per row (16 bytes each), reduced by shuffles.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void dsum_kernel(const T* __restrict__ dy, const T* __restrict__ out,
+                                                   float* __restrict__ dsum, long long rows) {
+    constexpr int EPL = 16 / sizeof(T);  // elements per lane
+    constexpr int LPR = D / EPL;         // lanes per row
+    const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = g / LPR;
+    const int part = (int)(g % LPR);
+    float acc = 0.0f;
+    if (row < rows) {
+        const u32x4 a = *(const u32x4*)(dy + row * D + part * EPL);
+        const u32x4 b = *(const u32x4*)(out + row * D + part * EPL);
+        if constexpr (sizeof(T) == 2) {
+            float x[8], y[8];
+            unpack8(a, x);
+            unpack8(b, y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc += __uint_as_float(a[e]) * __uint_as_float(b[e]);
+        }
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o /= 2) acc += __shfl_xor(acc, o, LPR);
+    if (row < rows && part == 0) dsum[row] = acc;
+}
+
+// Window [w0, w1) of the chunk of query row i (recurrent partition).
+__device__ __forceinline__ void row_window(const BwdParams& p, int i, int& w0, int& w1) {
+    const int t = i / (p.Tc * p.HW);
+    w0 = max(t * p.Tc - p.To, 0) * p.HW;
+    w1 = min((t + 1) * p.Tc, p.F) * p.HW;
+}
+
+// phi'(x) times the gradient of feature f (f < D: the elu+1 part, else the square part)
+template <int D>
+__device__ __forceinline__ float feature_grad(int f, float x, float g) {
+    return f < D ? elu1_grad(x) * g : 2.0f * x * g;
+}
+
+// Load 4 consecutive bf16 and return them as floats.
+__device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
+    const u32x2 w = *(const u32x2*)p;
+    f[0] = __uint_as_float(w[0] << 16);
+    f[1] = __uint_as_float(w[0] & 0xffff0000u);
+    f[2] = __uint_as_float(w[1] << 16);
+    f[3] = __uint_as_float(w[1] & 0xffff0000u);
+}
+
+// ------------------------------------------------------------------ dk / dv (bf16)
+template <int D, int PHI>
+__global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) {
+    constexpr int NW = kBwdWaves, BQ = kBwdQRows;
+    constexpr int C = D / 8, KS = D / 16, DT = D / 32;
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
+    constexpr int KSL = DP / 16, FT = DP / 32;
+    constexpr int QT = BQ * D;                         // elements of a Q (or dY) tile
+    constexpr int NI = QT * 2 / 1024;                  // 1 KB loads per tile
+    constexpr int OPW = 2 * NI / NW;                   // per wave, Q and dY
+    static_assert(2 * NI % NW == 0, "tile loads must split evenly");
+    __shared__ __attribute__((aligned(16))) uint16_t tiles_raw[2][2 * QT];
+    __shared__ __attribute__((aligned(16))) float rowf[2][2][BQ];   // lse, dsum
+    __shared__ __attribute__((aligned(16))) int roww[2][2][BQ];     // window bounds
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, lq = lane & 31;
+    const int nkb = (p.N + kBwdKeys - 1) / kBwdKeys;
+    const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    const int bh = item / nkb;
+    const int kb0 = (item - bh * nkb) * kBwdKeys;
+    const int key = kb0 + 32 * wave + lq;              // the lane's key (column of every tile)
+    const bool key_ok = key < p.N;
+    const int keyc = min(key, p.N - 1);
+
+    const uint16_t* qb = (const uint16_t*)p.q + bh * p.bh_stride;
+    const uint16_t* kbp = (const uint16_t*)p.k + bh * p.bh_stride;
+    const uint16_t* vbp = (const uint16_t*)p.v + bh * p.bh_stride;
+    const uint16_t* dyb = (const uint16_t*)p.dy + bh * p.bh_stride;
+    const float* lseb = p.lse + (long long)bh * p.N;
+    const float* dsb = p.dsum + (long long)bh * p.N;
+
+    bf16x8 kf[KS], vf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        kf[s] = __builtin_bit_cast(bf16x8, ldg_b128(kbp + (long long)keyc * D + 16 * s + 8 * h));
+        vf[s] = __builtin_bit_cast(bf16x8, ldg_b128(vbp + (long long)keyc * D + 16 * s + 8 * h));
+    }
+
+    // query rows of the chunks whose windows hold any of the block's keys
+    const int kl = min(kb0 + kBwdKeys, p.N) - 1;
+    const int fa = kb0 / p.HW, fb = kl / p.HW;
+    const int t_lo = fa / p.Tc, t_hi = min((fb + p.To) / p.Tc, p.C - 1);
+    const int qr0 = t_lo * p.Tc * p.HW;
+    const int qr1 = min((t_hi + 1) * p.Tc, p.F) * p.HW;
+    const int ntiles = (qr1 - qr0 + BQ - 1) / BQ;
+
+    const int rb = D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, qr1 * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t dyrs = __builtin_amdgcn_make_buffer_rsrc((void*)dyb, (short)0, qr1 * rb, 0x00020000);
+    auto load_tile = [&](int buf, int it) {
+        const int r0 = qr0 + it * BQ;
+#pragma unroll
+        for (int o = 0; o < OPW; ++o) {
+            const int op = wave + o * NW;
+            const bool isdy = op >= NI;
+            const int ins = isdy ? op - NI : op;
+            const int pos = 64 * ins + lane;
+            const int r = pos / C;
+            const int off = (r0 + r) * rb + ((pos % C) ^ swz<C>(r)) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isdy ? dyrs : qrs,
+                                                     (__attribute__((address_space(3))) void*)(
+                                                         (lds_u16*)tiles_raw[buf] + (isdy ? QT : 0) + 512 * ins),
+                                                     16, off, 0, 0, 0);
+        }
+    };
+    // per-row data of a tile: wave 0 loads it into registers, stores it later
+    float rl = 0.0f, rd = 0.0f;
+    int rw0 = 0, rw1 = 0;
+    auto fetch_rows = [&](int it) {
+        const int i = qr0 + it * BQ + lane;
+        if (i < qr1) {
+            rl = lseb[i];
+            rd = dsb[i];
+            row_window(p, i, rw0, rw1);
+        } else {
+            rl = rd = 0.0f;
+            rw0 = rw1 = 0;  // no key lies in an empty window
+        }
+    };
+    auto store_rows = [&](int buf) {
+        rowf[buf][0][lane] = rl;
+        rowf[buf][1][lane] = rd;
+        roww[buf][0][lane] = rw0;
+        roww[buf][1][lane] = rw1;
+    };
+
+    // transposing-read offsets (dY^T / Q^T fragments: lane row d = 32 c + lq,
+    // query rows 4h..4h+3 and 8+4h..8+4h+3 of a 16-row step)
+    const int tr_row = 4 * h + ((lane & 15) >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tr_sub = 4 * (lane & 1);
+    int toff[DT][2];
+#pragma unroll
+    for (int c = 0; c < DT; ++c) {
+        const int ch = 4 * c + tr_chunk;
+        toff[c][0] = tr_row * D + ((ch ^ swz<C>(tr_row)) << 3) + tr_sub;
+        toff[c][1] = (tr_row + 8) * D + ((ch ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
+    }
+
+    f32x16 dvt[DT], dkt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        dvt[dt] = f32x16{};
+        dkt[dt] = f32x16{};
+    }
+
+    if (ntiles > 0) {
+        load_tile(0, 0);
+        if (wave == 0) {
+            fetch_rows(0);
+            store_rows(0);
+        }
+    }
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        lds_barrier();
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            load_tile(buf ^ 1, it + 1);
+            if (wave == 0) fetch_rows(it + 1);
+        }
+        const lds_u16* Qs = (const lds_u16*)tiles_raw[buf];
+        const lds_u16* Ys = Qs + QT;
+#pragma unroll
+        for (int qs = 0; qs < BQ / 32; ++qs) {
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
+            const int arow = 32 * qs + lq;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
+                sacc = mfma32x32x16(lds_read_b128(Qs, off), kf[s], sacc);
+                pacc = mfma32x32x16(lds_read_b128(Ys, off), vf[s], pacc);
+            }
+            // rows 32 qs + 8 j + 4 h + i of the tile, column = the lane's key
+            u32x4 pw[2], dw[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = 32 * qs + 8 * j + 4 * h;
+                const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][0][r0];
+                const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][1][r0];
+                float pv[4], dv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int w0 = roww[buf][0][r0 + i], w1 = roww[buf][1][r0 + i];
+                    const bool in = key_ok && key >= w0 && key < w1;
+                    const float pe = in ? __builtin_amdgcn_exp2f((sacc[4 * j + i] - l4[i]) * kLog2e) : 0.0f;
+                    pv[i] = pe;
+                    dv[i] = pe * (pacc[4 * j + i] - d4[i]);
+                }
+                pw[j >> 1][2 * (j & 1)] = pack2_bf16(pv[0], pv[1]);
+                pw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(pv[2], pv[3]);
+                dw[j >> 1][2 * (j & 1)] = pack2_bf16(dv[0], dv[1]);
+                dw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(dv[2], dv[3]);
+            }
+            // dV^T += dY^T P, dK^T += Q^T dS over the subtile's 32 queries (two 16-row steps)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r16 = (32 * qs + 16 * kk) * D;
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
+                const bf16x8 db = __builtin_bit_cast(bf16x8, dw[kk]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x8 ya = cat(lds_read_tr(Ys, r16 + toff[dt][0]), lds_read_tr(Ys, r16 + toff[dt][1]));
+                    const bf16x8 qa = cat(lds_read_tr(Qs, r16 + toff[dt][0]), lds_read_tr(Qs, r16 + toff[dt][1]));
+                    dvt[dt] = mfma32x32x16(ya, pb, dvt[dt]);
+                    dkt[dt] = mfma32x32x16(qa, db, dkt[dt]);
+                }
+            }
+        }
+        if (more && wave == 0) store_rows(buf ^ 1);
+    }
+
+    // ---- linear branch of the wave's keys (delta blocks u <= C-2)
+    if constexpr (PHI != kPhiNone) {
+        if (p.lin) {
+            const int u_key = (keyc / p.HW + p.To) / p.Tc;
+            const int u_first = __builtin_amdgcn_readfirstlane(u_key);
+            const int u_last = __shfl(u_key, 31);
+            for (int u = u_first; u <= u_last && u <= p.C - 2; ++u) {
+                const bool mine = key_ok && u_key == u;
+                const long long sofs = (long long)bh * p.C * p.s_stride + (long long)u * p.s_stride;
+                const uint16_t* ghi = (const uint16_t*)p.g_hi + sofs;
+                const uint16_t* glo = (const uint16_t*)p.g_lo + sofs;
+                const uint16_t* gthi = (const uint16_t*)p.gt_hi + sofs;
+                const uint16_t* gtlo = (const uint16_t*)p.gt_lo + sofs;
+                const float* gz = p.gz + (long long)bh * p.C * p.z_stride + (long long)u * p.z_stride;
+                // dv += G_u^T phi(k): A = G_u^T rows (d), B = phi(k) (masked to the block's keys)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    f32x16 acc = f32x16{};
+#pragma unroll
+                    for (int ksl = 0; ksl < KSL; ++ksl) {
+                        float x[8], f[8];
+                        unpack8(__builtin_bit_cast(u32x4, kf[ksl % KS]), x);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) f[e] = mine ? (ksl < KS ? elu1(x[e]) : x[e] * x[e]) : 0.0f;
+                        u32x4 whi, wlo;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float h0 = round_bf16(f[2 * e]), h1 = round_bf16(f[2 * e + 1]);
+                            whi[e] = pack2_bf16(h0, h1);
+                            wlo[e] = pack2_bf16(f[2 * e] - h0, f[2 * e + 1] - h1);
+                        }
+                        const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
+                        const bf16x8 ah = __builtin_bit_cast(bf16x8, ldg_b128(ghi + off));
+                        const bf16x8 al = __builtin_bit_cast(bf16x8, ldg_b128(glo + off));
+                        const bf16x8 fh = __builtin_bit_cast(bf16x8, whi), fl = __builtin_bit_cast(bf16x8, wlo);
+                        acc = mfma32x32x16(ah, fh, acc);
+                        acc = mfma32x32x16(al, fh, acc);
+                        acc = mfma32x32x16(ah, fl, acc);
+                    }
+                    dvt[dt] += acc;
+                }
+                // dphi(k) = G_u v - g_u: A = G_u rows (features), B = V^T (the lane's key)
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) {
+                    f32x16 acc = f32x16{};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        const long long off = (long long)(32 * ft + lq) * D + 16 * s + 8 * h;
+                        acc = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(gthi + off)), vf[s], acc);
+                        acc = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(gtlo + off)), vf[s], acc);
+                    }
+                    if (!mine) continue;
+                    const int dt = ft % DT;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int f0 = 32 * ft + 8 * j + 4 * h;          // features f0 .. f0+3
+                        const int d0 = 32 * dt + 8 * j + 4 * h;          // their head_dim rows
+                        const f32x4 g4 = *(const f32x4*)(gz + f0);
+                        float kx[4];
+                        load4_bf16(kbp + (long long)keyc * D + d0, kx);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dkt[dt][4 * j + i] += feature_grad<D>(f0 + i, kx[i], acc[4 * j + i] - g4[i]);
+                    }
+                }
+            }
+        }
+    }
+
+    if (!key_ok) return;
+    uint16_t* dkp = (uint16_t*)p.dk + bh * p.bh_stride + (long long)key * D;
+    uint16_t* dvp = (uint16_t*)p.dv + bh * p.bh_stride + (long long)key * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = 32 * dt + 8 * j + 4 * h;
+            *(u32x2*)(dkp + d0) = u32x2{pack2_bf16(dkt[dt][4 * j], dkt[dt][4 * j + 1]),
+                                        pack2_bf16(dkt[dt][4 * j + 2], dkt[dt][4 * j + 3])};
+            *(u32x2*)(dvp + d0) = u32x2{pack2_bf16(dvt[dt][4 * j], dvt[dt][4 * j + 1]),
+                                        pack2_bf16(dvt[dt][4 * j + 2], dvt[dt][4 * j + 3])};
+        }
+}
+
+// ------------------------------------------------------------------ dq (bf16)
+template <int D, int PHI>
+__global__ __launch_bounds__(kBwdWaves * 64) void dq_bf16_kernel(BwdParams p, int tiles_per_chunk) {
+    constexpr int NW = kBwdWaves, BN = kBwdKTile;
+    constexpr int C = D / 8, KS = D / 16, DT = D / 32;
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
+    constexpr int FT = DP / 32;
+    constexpr int KT = BN * D;                          // elements of a K (or V) tile
+    constexpr int NI = KT * 2 / 1024;
+    constexpr int OPW = 2 * NI / NW;
+    static_assert(2 * NI % NW == 0, "tile loads must split evenly");
+    __shared__ __attribute__((aligned(16))) uint16_t tiles_raw[2][2 * KT];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, lq = lane & 31;
+    const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    const int per_bh = p.C * tiles_per_chunk;
+    const int bh = item / per_bh;
+    const int rem = item - bh * per_bh;
+    const int t = rem / tiles_per_chunk;
+    const int tile = rem - t * tiles_per_chunk;
+    const int q_end = min((t + 1) * p.Tc, p.F) * p.HW;
+    const int q0 = t * p.Tc * p.HW + tile * kBwdQueries;
+    if (q0 >= q_end) return;
+    const int w0 = max(t * p.Tc - p.To, 0) * p.HW;
+    const int nkeys = q_end - w0;
+    const int ntiles = (nkeys + BN - 1) / BN;
+    const int row = q0 + 32 * wave + lq;                 // the lane's query
+    const bool row_ok = row < q_end;
+    const int rowc = min(row, q_end - 1);
+
+    const uint16_t* qb = (const uint16_t*)p.q + bh * p.bh_stride;
+    const uint16_t* dyb = (const uint16_t*)p.dy + bh * p.bh_stride;
+    const uint16_t* kbp = (const uint16_t*)p.k + bh * p.bh_stride + (long long)w0 * D;
+    const uint16_t* vbp = (const uint16_t*)p.v + bh * p.bh_stride + (long long)w0 * D;
+    const float lse = p.lse[(long long)bh * p.N + rowc];
+    const float dsum = p.dsum[(long long)bh * p.N + rowc];
+    const float lse2 = lse * kLog2e;
+
+    bf16x8 qf[KS], yf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        qf[s] = __builtin_bit_cast(bf16x8, ldg_b128(qb + (long long)rowc * D + 16 * s + 8 * h));
+        yf[s] = __builtin_bit_cast(bf16x8, ldg_b128(dyb + (long long)rowc * D + 16 * s + 8 * h));
+    }
+
+    const int rb = D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbp, (short)0, nkeys * rb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbp, (short)0, nkeys * rb, 0x00020000);
+    auto load_tile = [&](int buf, int it) {
+#pragma unroll
+        for (int o = 0; o < OPW; ++o) {
+            const int op = wave + o * NW;
+            const bool isv = op >= NI;
+            const int ins = isv ? op - NI : op;
+            const int pos = 64 * ins + lane;
+            const int r = pos / C;
+            const int off = (it * BN + r) * rb + ((pos % C) ^ swz<C>(r)) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs,
+                                                     (__attribute__((address_space(3))) void*)(
+                                                         (lds_u16*)tiles_raw[buf] + (isv ? KT : 0) + 512 * ins),
+                                                     16, off, 0, 0, 0);
+        }
+    };
+    const int tr_row = 4 * h + ((lane & 15) >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tr_sub = 4 * (lane & 1);
+    int toff[DT][2];
+#pragma unroll
+    for (int c = 0; c < DT; ++c) {
+        const int ch = 4 * c + tr_chunk;
+        toff[c][0] = tr_row * D + ((ch ^ swz<C>(tr_row)) << 3) + tr_sub;
+        toff[c][1] = (tr_row + 8) * D + ((ch ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
+    }
+
+    f32x16 dqt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dqt[dt] = f32x16{};
+
+    if (ntiles > 0) load_tile(0, 0);
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        lds_barrier();
+        if (it + 1 < ntiles) load_tile(buf ^ 1, it + 1);
+        const lds_u16* Ks = (const lds_u16*)tiles_raw[buf];
+        const lds_u16* Vs = Ks + KT;
+#pragma unroll
+        for (int ks = 0; ks < BN / 32; ++ks) {
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
+            const int arow = 32 * ks + lq;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
+                sacc = mfma32x32x16(lds_read_b128(Ks, off), qf[s], sacc);
+                pacc = mfma32x32x16(lds_read_b128(Vs, off), yf[s], pacc);
+            }
+            // key rows 32 ks + 8 j + 4 h + i of the tile, column = the lane's query
+            u32x4 dw[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float dv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kr = it * BN + 32 * ks + 8 * j + 4 * h + i;
+                    const float pe = kr < nkeys ? __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - lse2) : 0.0f;
+                    dv[i] = pe * (pacc[4 * j + i] - dsum);
+                }
+                dw[j >> 1][2 * (j & 1)] = pack2_bf16(dv[0], dv[1]);
+                dw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(dv[2], dv[3]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r16 = (32 * ks + 16 * kk) * D;
+                const bf16x8 db = __builtin_bit_cast(bf16x8, dw[kk]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x8 ka = cat(lds_read_tr(Ks, r16 + toff[dt][0]), lds_read_tr(Ks, r16 + toff[dt][1]));
+                    dqt[dt] = mfma32x32x16(ka, db, dqt[dt]);
+                }
+            }
+        }
+    }
+
+    // ---- linear branch: dphi(q) = e^{-lse} (S_t dy - D z_t)
+    if constexpr (PHI != kPhiNone) {
+        if (p.lin && t * p.Tc - p.To > 0) {
+            const long long sofs = (long long)bh * p.C * p.s_stride + (long long)t * p.s_stride;
+            const uint16_t* sthi = (const uint16_t*)p.st_hi + sofs;
+            const uint16_t* stlo = (const uint16_t*)p.st_lo + sofs;
+            const float* zt = p.z + (long long)bh * p.C * p.z_stride + (long long)t * p.z_stride;
+            const float el = __expf(-lse);
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) {
+                f32x16 acc = f32x16{};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const long long off = (long long)(32 * ft + lq) * D + 16 * s + 8 * h;
+                    acc = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(sthi + off)), yf[s], acc);
+                    acc = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(stlo + off)), yf[s], acc);
+                }
+                const int dt = ft % DT;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int f0 = 32 * ft + 8 * j + 4 * h;
+                    const int d0 = 32 * dt + 8 * j + 4 * h;
+                    const f32x4 z4 = *(const f32x4*)(zt + f0);
+                    float qx[4];
+                    load4_bf16(qb + (long long)rowc * D + d0, qx);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dqt[dt][4 * j + i] += feature_grad<D>(f0 + i, qx[i], el * (acc[4 * j + i] - dsum * z4[i]));
+                }
+            }
+        }
+    }
+
+    if (!row_ok) return;
+    uint16_t* dqp = (uint16_t*)p.dq + bh * p.bh_stride + (long long)row * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = 32 * dt + 8 * j + 4 * h;
+            *(u32x2*)(dqp + d0) = u32x2{pack2_bf16(dqt[dt][4 * j], dqt[dt][4 * j + 1]),
+                                        pack2_bf16(dqt[dt][4 * j + 2], dqt[dt][4 * j + 3])};
+        }
+}
+
+// ------------------------------------------------------------------ fp32
+constexpr int kF32Lanes = 64;
+
+// dk, dv: one key per lane; query rows of the chunks whose windows hold the
+// workgroup's keys stream through LDS 32 at a time.
+template <int D, int PHI>
+__global__ __launch_bounds__(kF32Lanes) void dkdv_f32_kernel(BwdParams p) {
+    constexpr int R = 32;
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
+    __shared__ float Qs[R][D], Ys[R][D];
+    __shared__ float Ls[R], Ds[R];
+    __shared__ int W0[R], W1[R];
+    const int nkb = (p.N + kF32Lanes - 1) / kF32Lanes;
+    const int bh = blockIdx.x / nkb;
+    const int kb0 = (blockIdx.x - bh * nkb) * kF32Lanes;
+    const int tid = threadIdx.x;
+    const int key = kb0 + tid;
+    const bool key_ok = key < p.N;
+    const int keyc = min(key, p.N - 1);
+    const float* qb = (const float*)p.q + bh * p.bh_stride;
+    const float* kb = (const float*)p.k + bh * p.bh_stride;
+    const float* vb = (const float*)p.v + bh * p.bh_stride;
+    const float* yb = (const float*)p.dy + bh * p.bh_stride;
+    float k[D], v[D], dk[D], dv[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        k[c] = kb[(long long)keyc * D + c];
+        v[c] = vb[(long long)keyc * D + c];
+        dk[c] = 0.0f;
+        dv[c] = 0.0f;
+    }
+    const int kl = min(kb0 + kF32Lanes, p.N) - 1;
+    const int t_lo = (kb0 / p.HW) / p.Tc, t_hi = min((kl / p.HW + p.To) / p.Tc, p.C - 1);
+    const int qr0 = t_lo * p.Tc * p.HW, qr1 = min((t_hi + 1) * p.Tc, p.F) * p.HW;
+    for (int r0 = qr0; r0 < qr1; r0 += R) {
+        __syncthreads();
+        for (int e = tid; e < R * D; e += kF32Lanes) {
+            const int r = e / D, c = e % D;
+            const int i = r0 + r;
+            Qs[r][c] = i < qr1 ? qb[(long long)i * D + c] : 0.0f;
+            Ys[r][c] = i < qr1 ? yb[(long long)i * D + c] : 0.0f;
+        }
+        if (tid < R) {
+            const int i = r0 + tid;
+            int a = 0, b = 0;
+            if (i < qr1) row_window(p, i, a, b);
+            Ls[tid] = i < qr1 ? p.lse[(long long)bh * p.N + i] : 0.0f;
+            Ds[tid] = i < qr1 ? p.dsum[(long long)bh * p.N + i] : 0.0f;
+            W0[tid] = a;
+            W1[tid] = b;
+        }
+        __syncthreads();
+        for (int r = 0; r < R; ++r) {
+            if (!(key_ok && key >= W0[r] && key < W1[r])) continue;
+            float s = 0.0f, dp = 0.0f;
+#pragma unroll
+            for (int c = 0; c < D; ++c) {
+                s = fmaf(Qs[r][c], k[c], s);
+                dp = fmaf(Ys[r][c], v[c], dp);
+            }
+            const float pe = expf(s - Ls[r]);
+            const float ds = pe * (dp - Ds[r]);
+#pragma unroll
+            for (int c = 0; c < D; ++c) {
+                dv[c] = fmaf(pe, Ys[r][c], dv[c]);
+                dk[c] = fmaf(ds, Qs[r][c], dk[c]);
+            }
+        }
+    }
+    if (!key_ok) return;
+    if (PHI != kPhiNone && p.lin) {
+        const int u = (key / p.HW + p.To) / p.Tc;
+        if (u <= p.C - 2) {
+            const long long sofs = (long long)bh * p.C * p.s_stride + (long long)u * p.s_stride;
+            const float* G = (const float*)p.gt_hi + sofs;   // [D'][d]
+            const float* gz = p.gz + (long long)bh * p.C * p.z_stride + (long long)u * p.z_stride;
+            for (int f = 0; f < DP; ++f) {
+                const float x = k[f % D];
+                const float phi = f < D ? elu1(x) : x * x;
+                float g = -gz[f];
+#pragma unroll
+                for (int c = 0; c < D; ++c) {
+                    g = fmaf(G[(long long)f * D + c], v[c], g);
+                    dv[c] = fmaf(G[(long long)f * D + c], phi, dv[c]);
+                }
+                dk[f % D] += feature_grad<D>(f, x, g);
+            }
+        }
+    }
+    float* dkp = (float*)p.dk + bh * p.bh_stride + (long long)key * D;
+    float* dvp = (float*)p.dv + bh * p.bh_stride + (long long)key * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        dkp[c] = dk[c];
+        dvp[c] = dv[c];
+    }
+}
+
+// dq: one query per lane; the window's keys stream through LDS 32 at a time.
+template <int D, int PHI>
+__global__ __launch_bounds__(kF32Lanes) void dq_f32_kernel(BwdParams p, int tiles_per_chunk) {
+    constexpr int R = 32;
+    constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
+    __shared__ float Ks[R][D], Vs[R][D];
+    const int per_bh = p.C * tiles_per_chunk;
+    const int bh = blockIdx.x / per_bh;
+    const int rem = blockIdx.x - bh * per_bh;
+    const int t = rem / tiles_per_chunk;
+    const int tile = rem - t * tiles_per_chunk;
+    const int q_end = min((t + 1) * p.Tc, p.F) * p.HW;
+    const int q0 = t * p.Tc * p.HW + tile * kF32Lanes;
+    if (q0 >= q_end) return;
+    const int tid = threadIdx.x;
+    const int row = q0 + tid;
+    const bool row_ok = row < q_end;
+    const int rowc = min(row, q_end - 1);
+    const int w0 = max(t * p.Tc - p.To, 0) * p.HW;
+    const float* qb = (const float*)p.q + bh * p.bh_stride;
+    const float* kb = (const float*)p.k + bh * p.bh_stride;
+    const float* vb = (const float*)p.v + bh * p.bh_stride;
+    const float* yb = (const float*)p.dy + bh * p.bh_stride;
+    float q[D], y[D], dq[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        q[c] = qb[(long long)rowc * D + c];
+        y[c] = yb[(long long)rowc * D + c];
+        dq[c] = 0.0f;
+    }
+    const float lse = p.lse[(long long)bh * p.N + rowc];
+    const float dsum = p.dsum[(long long)bh * p.N + rowc];
+    for (int j0 = w0; j0 < q_end; j0 += R) {
+        __syncthreads();
+        for (int e = tid; e < R * D; e += kF32Lanes) {
+            const int r = e / D, c = e % D;
+            const int j = j0 + r;
+            Ks[r][c] = j < q_end ? kb[(long long)j * D + c] : 0.0f;
+            Vs[r][c] = j < q_end ? vb[(long long)j * D + c] : 0.0f;
+        }
+        __syncthreads();
+        for (int r = 0; r < R && j0 + r < q_end; ++r) {
+            float s = 0.0f, dp = 0.0f;
+#pragma unroll
+            for (int c = 0; c < D; ++c) {
+                s = fmaf(q[c], Ks[r][c], s);
+                dp = fmaf(y[c], Vs[r][c], dp);
+            }
+            const float ds = expf(s - lse) * (dp - dsum);
+#pragma unroll
+            for (int c = 0; c < D; ++c) dq[c] = fmaf(ds, Ks[r][c], dq[c]);
+        }
+    }
+    if (!row_ok) return;
+    if (PHI != kPhiNone && p.lin && t * p.Tc - p.To > 0) {
+        const long long sofs = (long long)bh * p.C * p.s_stride + (long long)t * p.s_stride;
+        const float* S = (const float*)p.st_hi + sofs;   // [D'][d]
+        const float* zt = p.z + (long long)bh * p.C * p.z_stride + (long long)t * p.z_stride;
+        const float el = expf(-lse);
+        for (int f = 0; f < DP; ++f) {
+            float g = -dsum * zt[f];
+#pragma unroll
+            for (int c = 0; c < D; ++c) g = fmaf(S[(long long)f * D + c], y[c], g);
+            dq[f % D] += feature_grad<D>(f, q[f % D], el * g);
+        }
+    }
+    float* dqp = (float*)p.dq + bh * p.bh_stride + (long long)row * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) dqp[c] = dq[c];
+}
+
+int dq_tiles_per_chunk(const BwdParams& p, int rows) {
+    const long long chunk_rows = (long long)min(p.Tc, p.F) * p.HW;
+    return (int)((chunk_rows + rows - 1) / rows);
+}
+
+template <int D, int PHI>
+hipError_t launch_bf16_dp(const BwdParams& p, hipStream_t s) {
+    const long long kblocks = (long long)p.BH * ((p.N + kBwdKeys - 1) / kBwdKeys);
+    const int tpc = dq_tiles_per_chunk(p, kBwdQueries);
+    const long long qblocks = (long long)p.BH * p.C * tpc;
+    if (kblocks > 0) dkdv_bf16_kernel<D, PHI><<<(unsigned)kblocks, kBwdWaves * 64, 0, s>>>(p);
+    if (qblocks > 0) dq_bf16_kernel<D, PHI><<<(unsigned)qblocks, kBwdWaves * 64, 0, s>>>(p, tpc);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(const BwdParams& p, hipStream_t s) {
+    switch (p.phi) {
+    case kPhiNone: return launch_bf16_dp<D, kPhiNone>(p, s);
+    case kPhiElu1: return launch_bf16_dp<D, kPhiElu1>(p, s);
+    case kPhiPoly2: return launch_bf16_dp<D, kPhiPoly2>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D, int PHI>
+hipError_t launch_f32_dp(const BwdParams& p, hipStream_t s) {
+    const long long kblocks = (long long)p.BH * ((p.N + kF32Lanes - 1) / kF32Lanes);
+    const int tpc = dq_tiles_per_chunk(p, kF32Lanes);
+    const long long qblocks = (long long)p.BH * p.C * tpc;
+    if (kblocks > 0) dkdv_f32_kernel<D, PHI><<<(unsigned)kblocks, kF32Lanes, 0, s>>>(p);
+    if (qblocks > 0) dq_f32_kernel<D, PHI><<<(unsigned)qblocks, kF32Lanes, 0, s>>>(p, tpc);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_d(const BwdParams& p, hipStream_t s) {
+    switch (p.phi) {
+    case kPhiNone: return launch_f32_dp<D, kPhiNone>(p, s);
+    case kPhiElu1: return launch_f32_dp<D, kPhiElu1>(p, s);
+    case kPhiPoly2: return launch_f32_dp<D, kPhiPoly2>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+template <typename T>
+static hipError_t dsum_typed(const BwdParams& p, float* dsum, hipStream_t s) {
+    const long long rows = (long long)p.BH * p.N;
+    const int epl = 16 / (int)sizeof(T);
+    const long long threads = rows * (p.d / epl);
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    switch (p.d) {
+    case 16: dsum_kernel<16, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
+    case 32: dsum_kernel<32, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
+    case 64: dsum_kernel<64, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
+    case 128: dsum_kernel<128, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dsum(const BwdParams& p, float* dsum, bool bf16, hipStream_t s) {
+    return bf16 ? dsum_typed<uint16_t>(p, dsum, s) : dsum_typed<float>(p, dsum, s);
+}
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
+    switch (p.d) {
+    case 32: return launch_bf16_d<32>(p, s);
+    case 64: return launch_bf16_d<64>(p, s);
+    case 128: return launch_bf16_d<128>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s) {
+    switch (p.d) {
+    case 16: return launch_f32_d<16>(p, s);
+    case 32: return launch_f32_d<32>(p, s);
+    case 64: return launch_f32_d<64>(p, s);
+    case 128: return launch_f32_d<128>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace rehyat

@@ -111,15 +111,17 @@ __global__ __launch_bounds__(kF32Rows) void local_f32_kernel(LocalParams p) {
         }
     }
     if (!valid) return;
-    float cs = 1.0f, cl = 0.0f;
+    float cs = 1.0f, cl = 0.0f, M = m;
     if (PHI != kPhiNone && lin && nl > 0.0f) {
-        const float M = fmaxf(m, logf(nl));
+        M = fmaxf(m, logf(nl));
         cs = expf(m - M);
         cl = expf(-M);
     }
-    const float inv = 1.0f / (cs * l + cl * nl);
+    const float den = cs * l + cl * nl;  // (n^S + n^L) e^-M
+    const float inv = 1.0f / den;
     const bool partials = p.pm || p.pnt || p.poS || p.poL || p.pnL;
     const long long prow = bh * (long long)(p.bh_stride / D) + row;
+    if (p.lse) p.lse[prow] = M + logf(den);
     if (!partials) {
         float* ob = (float*)p.out + bh * p.bh_stride + (long long)row * D;
 #pragma unroll
@@ -142,7 +144,9 @@ __global__ __launch_bounds__(kF32Rows) void local_f32_kernel(LocalParams p) {
     }
 }
 
-template <int D, int PHI>
+// GRAD: the backward's gradient sums (row r's phi scaled by exp(-lse_r), its
+// z weight dsum_r; the second operand is dy)
+template <int D, int PHI, bool GRAD = false>
 __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
     constexpr int BN = 32;
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
@@ -150,6 +154,7 @@ __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
     constexpr int PER = (SE + 255) / 256;
     __shared__ float Fs[BN][DP];
     __shared__ float Vs[BN][D];
+    __shared__ float Zw[BN];
 
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;
@@ -200,6 +205,15 @@ __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
             }
             Vs[r][c] = vv;
         }
+        if (GRAD) {  // scale phi by exp(-lse) per row; z weights dsum
+            __syncthreads();
+            for (int x = tid; x < BN * DP; x += 256) {
+                const int r = x / DP, c = x % DP;
+                const int j = min(base + r, j1 - 1);
+                Fs[r][c] *= expf(-p.row_lse[bh * (p.bh_stride / D) + j]);
+            }
+            if (tid < BN) Zw[tid] = p.row_d[bh * (p.bh_stride / D) + min(base + tid, j1 - 1)];
+        }
         if (PHI == kPhiFeat) {  // precomputed phi(k) rows
             for (int x = tid; x < BN * DP; x += 256) {
                 const int r = x / DP, c = x % DP;
@@ -224,7 +238,7 @@ __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
         }
         if (tid < DP) {
 #pragma unroll 8
-            for (int r = 0; r < BN; ++r) zacc += Fs[r][tid];
+            for (int r = 0; r < BN; ++r) zacc += GRAD ? Fs[r][tid] * Zw[r] : Fs[r][tid];
         }
         __syncthreads();
     }
@@ -255,8 +269,14 @@ hipError_t launch_state_d(const StateParams& p, hipStream_t s) {
     const int blocks = p.BH * p.n_blocks * p.n_sub;
     if (blocks <= 0) return hipSuccess;
     switch (p.phi) {
-    case kPhiElu1: state_f32_kernel<D, kPhiElu1><<<blocks, 256, 0, s>>>(p); break;
-    case kPhiPoly2: state_f32_kernel<D, kPhiPoly2><<<blocks, 256, 0, s>>>(p); break;
+    case kPhiElu1:
+        if (p.row_lse) state_f32_kernel<D, kPhiElu1, true><<<blocks, 256, 0, s>>>(p);
+        else state_f32_kernel<D, kPhiElu1><<<blocks, 256, 0, s>>>(p);
+        break;
+    case kPhiPoly2:
+        if (p.row_lse) state_f32_kernel<D, kPhiPoly2, true><<<blocks, 256, 0, s>>>(p);
+        else state_f32_kernel<D, kPhiPoly2><<<blocks, 256, 0, s>>>(p);
+        break;
     case kPhiFeat: state_f32_kernel<D, kPhiFeat><<<blocks, 256, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }

@@ -27,11 +27,18 @@ inline int feature_dim(int phi, int d) {
 //   T_o div T_c (clipped at block 0), and ends at the start of block 2t+3, so
 //   its linear set (every key outside the window) is the blocks before
 //   max(2(t - q), 0) plus the blocks from 2t+3 on.
-enum BlockMode { kCausal = 0, kBidirectional = 1 };
+//  kChunkRows (backward): block u = the frames of chunk u+1, u = 0 .. C-2
+//   (the queries whose gradient sums feed the keys of the earlier delta blocks).
+enum BlockMode { kCausal = 0, kBidirectional = 1, kChunkRows = 2 };
 
-__host__ __device__ inline int state_block_count(int mode, int C) { return mode == kCausal ? C - 1 : 2 * C + 1; }
+__host__ __device__ inline int state_block_count(int mode, int C) { return mode == kBidirectional ? 2 * C + 1 : C - 1; }
 
 __host__ __device__ inline void state_block_frames(int mode, int u, int Tc, int To, int F, int& f0, int& f1) {
+    if (mode == kChunkRows) {
+        f0 = (u + 1) * Tc < F ? (u + 1) * Tc : F;
+        f1 = (u + 2) * Tc < F ? (u + 2) * Tc : F;
+        return;
+    }
     if (mode == kCausal) {
         f0 = u * Tc - To > 0 ? u * Tc - To : 0;
         f1 = (u + 1) * Tc - To > 0 ? (u + 1) * Tc - To : 0;
@@ -82,6 +89,8 @@ struct LocalParams {
     // kPhiFeat: phi(q) rows, [BH][n_rows][2d] in the input dtype (row = query row)
     const void* fq;
     long long fq_bh_stride;
+    // optional: ln(n^S + n^L) per query, fp32 [BH][n_rows] (the backward's normaliser)
+    float* lse;
 };
 
 // Key tiles of BN keys that a query tile of chunk t streams (its softmax window).
@@ -147,6 +156,9 @@ struct StateParams {
     // overlap segment [BH][prev rows][2d] (indexed like k and kp)
     const void* fk; const void* fkp;
     long long fk_bh_stride, fkp_bh_stride;
+    // backward (kChunkRows): row r contributes c_r phi(x_r) v_r^T to S and
+    // D_r c_r phi(x_r) to z, c_r = exp(-row_lse[r]), D_r = row_d[r] ([BH][n_rows])
+    const float* row_lse; const float* row_d;
 };
 
 // Scan: X_0 = init (or 0); X_{u+1} = X_u + sum_p partial[u][p].  Writes the
@@ -166,6 +178,28 @@ struct ScanParams {
     // before max(2(t - q), 0) plus the blocks from 2t+3 on (q = T_o div T_c)
     int mode, C, q;
     float* suffix;                    // [BH][C][E] fp32 scratch for the suffix sums
+    // kChunkRows (backward): slot u gets the sum of the blocks u .. U-1
+    // optional copy of each prepared S^T transposed, [D'][d] (bf16 hi/lo, or fp32 in t_hi)
+    void* t_hi; void* t_lo;
+};
+
+// Backward of the hybrid attention (per-chunk windows of the recurrent form).
+// dq, dk, dv in the input dtype.  lse = ln(n^S + n^L) and dsum = dy.y per query.
+struct BwdParams {
+    const void* q; const void* k; const void* v; const void* dy;  // [BH][N][d]
+    const void* out;                                              // forward output (for dsum)
+    const float* lse; const float* dsum;                          // [BH][N]
+    void* dq; void* dk; void* dv;
+    long long bh_stride;                                          // N * d
+    int N, HW, F, Tc, To, C, BH, d, phi;
+    // linear branch, per chunk t: the forward state S_t prepared transposed
+    // ([D'][d], bf16 hi/lo or fp32) and z_t; per delta block u: the suffix of
+    // the gradient sums, G_u = sum_{t>u} sum_{i in chunk t} e^{-lse_i} phi(q_i) dy_i^T,
+    // prepared as G_u^T [d][D'] and G_u [D'][d], and g_u = sum e^{-lse_i} dsum_i phi(q_i)
+    const void* st_hi; const void* st_lo; const float* z;
+    const void* g_hi; const void* g_lo; const void* gt_hi; const void* gt_lo; const float* gz;
+    long long s_stride, z_stride;     // per chunk / per block: d*D' and D' elements (bh stride = C times)
+    int lin;                          // the linear branch is active (some chunk has a linear set)
 };
 
 // Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot
@@ -207,6 +241,9 @@ hipError_t launch_state_f32(const StateParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s);
 hipError_t launch_phi_mlp_bf16(const MlpParams& p, hipStream_t s);
+hipError_t launch_bwd_dsum(const BwdParams& p, float* dsum, bool bf16, hipStream_t s);  // dsum = rowwise dy . out
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);   // dq, dk, dv
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_phi_mlp_f32(const MlpParams& p, hipStream_t s);
 bool phi_mlp_hidden_ok(int hidden);  // hidden widths the MLP kernels are built for
 

@@ -135,17 +135,19 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
         }
         nl = xhalf_sum(nlp);
     }
-    float cs = 1.0f, cl = 0.0f;
+    float cs = 1.0f, cl = 0.0f, M2 = m2;
     if (lin && nl > 0.0f) {
-        const float M2 = fmaxf(m2, __builtin_amdgcn_logf(nl));
+        M2 = fmaxf(m2, __builtin_amdgcn_logf(nl));
         cs = __builtin_amdgcn_exp2f(m2 - M2);
         cl = __builtin_amdgcn_exp2f(-M2);
     }
-    const float inv = 1.0f / (cs * lsum + cl * nl);
+    const float den = cs * lsum + cl * nl;  // (n^S + n^L) 2^-M2
+    const float inv = 1.0f / den;
     const bool store_out =
         p.pm == nullptr && p.poS == nullptr && p.poL == nullptr && p.pnt == nullptr && p.pnL == nullptr;
     const bool valid = row < q_end;  // rows past the chunk end hold duplicated queries
     const long long prow = bh * (long long)(p.bh_stride / D) + row;
+    if (p.lse && valid && h == 0) p.lse[prow] = kLn2 * (M2 + __builtin_amdgcn_logf(den));
     if (!store_out && valid && h == 0) {
         if (p.pm) p.pm[prow] = mtrue;
         if (p.pnt) p.pnt[prow] = lsum * __builtin_amdgcn_exp2f(m2 - mtrue * kLog2e);

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
         if (t < p.t_first) return;
         const int slot = t - p.t_offset;
         if (e4 < SE) {
-            const long long off = (long long)bh * p.s_bh_stride + (long long)slot * p.s_chunk_stride + e4;
+            const long long base = (long long)bh * p.s_bh_stride + (long long)slot * p.s_chunk_stride;
+            const long long off = base + e4;
             if (p.f32_prep) {
                 *(f32x4*)((float*)p.s_hi + off) = x;
             } else {
@@ -46,6 +47,20 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
                 *(u32x2*)((uint16_t*)p.s_hi + off) = u32x2{hi[0], hi[1]};
                 *(u32x2*)((uint16_t*)p.s_lo + off) = u32x2{lo[0], lo[1]};
             }
+            if (p.t_hi) {  // the transposed copy: element (r, c) of [d][D'] goes to (c, r) of [D'][d]
+                const int r = e4 / p.Dp, c = e4 - r * p.Dp;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const long long to = base + (long long)(c + i) * p.d + r;
+                    if (p.f32_prep) {
+                        ((float*)p.t_hi)[to] = x[i];
+                    } else {
+                        const float hv = round_bf16(x[i]);
+                        ((__bf16*)p.t_hi)[to] = (__bf16)hv;
+                        ((__bf16*)p.t_lo)[to] = (__bf16)(x[i] - hv);
+                    }
+                }
+            }
         } else {
             const long long off = (long long)bh * p.z_bh_stride + (long long)slot * p.z_chunk_stride + (e4 - SE);
             *(f32x4*)(p.z + off) = x;
@@ -56,6 +71,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
         for (int sp = 0; sp < p.n_sub; ++sp) d += *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
         return d;
     };
+    if (p.mode == kChunkRows) {
+        // suffix sums: slot u gets the blocks u .. U-1
+        for (int u = p.U - 1; u >= 0; --u) {
+            x += block_sum(u);
+            emit(u);
+        }
+        return;
+    }
     if (p.mode == kBidirectional) {
         // suffix sums Y_k = sum of blocks k.. U-1, backwards; chunk t needs
         // Y_{2t+3} (zero past the last block).  Each thread keeps its own 4

@@ -82,7 +82,9 @@ constexpr int state_nw(int d, int phi) {
     return phi == kPhiFeat && d == 32 ? 4 : state_waves(phi == kPhiElu1 ? d : 2 * d);
 }
 
-template <int D, int PHI>
+// GRAD: the backward's gradient sums (rows are queries of a chunk, the second
+// operand is dy; row r's phi is scaled by exp(-lse_r) and its z weight is dsum_r)
+template <int D, int PHI, bool GRAD = false>
 __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(StateParams p) {
     constexpr bool FEAT = PHI == kPhiFeat;            // phi(k) rows come precomputed
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
@@ -155,6 +157,8 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
     auto load_tile = [&](lds_u16* base, int t) {
         state_load_tile<D, KW, BN, NW, OPW>(base, wave, lane, j0 + t * BN, prev_rows, krs, vrs, kprs, vprs);
     };
+    const float* glse = GRAD ? p.row_lse + bh * (p.bh_stride / D) : nullptr;
+    const float* gdsum = GRAD ? p.row_d + bh * (p.bh_stride / D) : nullptr;
 
     // transposing-read addressing (see lds_read_tr): for its column, lane
     // (half h) receives keys 4h..4h+3 of the first read and 8+4h..8+4h+3 of
@@ -203,6 +207,15 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
             for (int dt = 0; dt < DT; ++dt)
                 a[dt] = cat(lds_read_tr(Vs, r16 + toff[dt][0]), lds_read_tr(Vs, r16 + toff[dt][1]));
             const int kbase = t * BN + 16 * ks + 4 * h;  // key of element 0 (elements 4..7: +8)
+            float gc[GRAD ? 8 : 1], gd[GRAD ? 8 : 1];  // per-row scale and z weight (backward)
+            if constexpr (GRAD) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = j0 + min(kbase + (e < 4 ? e : e + 4), nkeys - 1);  // clip row, clamped
+                    gc[e] = __expf(-glse[r]);
+                    gd[e] = gdsum[r];
+                }
+            }
             if constexpr (FEAT) {
                 // phi(k) is already bf16: one MFMA per output tile, no split
 #pragma unroll
@@ -241,7 +254,12 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
                     const int key = kbase + (e < 4 ? e : e + 4);
                     const float y = square ? x * x : elu1(x);
                     f[e] = !TAIL || key < nkeys ? y : 0.0f;
-                    zpart[i] += f[e];
+                    if constexpr (GRAD) {
+                        f[e] *= gc[e];
+                        zpart[i] += f[e] * gd[e];
+                    } else {
+                        zpart[i] += f[e];
+                    }
                 }
                 u32x4 whi, wlo;
 #pragma unroll
@@ -326,8 +344,14 @@ hipError_t launch_d(const StateParams& p, hipStream_t s) {
     const long long blocks = (long long)p.BH * p.n_blocks * p.n_sub;
     if (blocks <= 0) return hipSuccess;
     switch (p.phi) {
-    case kPhiElu1: state_bf16_kernel<D, kPhiElu1><<<(unsigned)blocks, state_nw(D, kPhiElu1) * 64, 0, s>>>(p); break;
-    case kPhiPoly2: state_bf16_kernel<D, kPhiPoly2><<<(unsigned)blocks, state_nw(D, kPhiPoly2) * 64, 0, s>>>(p); break;
+    case kPhiElu1:
+        if (p.row_lse) state_bf16_kernel<D, kPhiElu1, true><<<(unsigned)blocks, state_nw(D, kPhiElu1) * 64, 0, s>>>(p);
+        else state_bf16_kernel<D, kPhiElu1><<<(unsigned)blocks, state_nw(D, kPhiElu1) * 64, 0, s>>>(p);
+        break;
+    case kPhiPoly2:
+        if (p.row_lse) state_bf16_kernel<D, kPhiPoly2, true><<<(unsigned)blocks, state_nw(D, kPhiPoly2) * 64, 0, s>>>(p);
+        else state_bf16_kernel<D, kPhiPoly2><<<(unsigned)blocks, state_nw(D, kPhiPoly2) * 64, 0, s>>>(p);
+        break;
     case kPhiFeat: state_bf16_kernel<D, kPhiFeat><<<(unsigned)blocks, state_nw(D, kPhiFeat) * 64, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }

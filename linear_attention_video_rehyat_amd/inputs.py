@@ -98,6 +98,14 @@ def make_qkv(w: Workload, device="cpu"):
     return tuple(out)
 
 
+def make_dout(w: Workload, device="cpu"):
+    """Seeded output gradient dy ~ N(0, 1) [B, H, N, d] in the workload dtype
+    (seed default_rng(1000*seed_id + 5))."""
+    x = _draw(1000 * w.seed_id + 5, (w.B, w.H, w.N, w.head_dim))
+    t = torch.from_numpy(x).to(w.torch_dtype)
+    return t.to(device) if device != "cpu" else t
+
+
 def custom(B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
            dtype="bf16", seed_id=100, key_scale=None) -> Workload:
     """An ad-hoc workload (tests: ragged tails, odd geometries)."""
