@@ -148,6 +148,39 @@ def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=Tru
     return res
 
 
+def backward_bench(rh, inputs, q, k, v, w, Tc, To, phi, steps, cnt):
+    """Training direction at the same shape: forward with lse, then the
+    backward (dq, dk, dv) for a seeded output gradient, timed with torch events
+    on the current stream.  The softmax-window part of the backward does 5
+    GEMM-shaped products per (query, window key) pair where the forward does 2,
+    plus the recomputation of QK^T in both the dk/dv and the dq kernels: its
+    algorithmic work is counted as 2.5x the forward's softmax FLOPs (the usual
+    convention for attention backward)."""
+    import torch
+    dy = inputs.make_dout(w).to(q.device)
+    out, lse = rh.attn_fwd_lse(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    for _ in range(2):
+        rh.attn_bwd(q, k, v, out, lse, dy, w.frames, w.tokens_per_frame, Tc, To, phi, grads=grads)
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(steps):
+        rh.attn_fwd_lse(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out, lse=lse)
+    e1.record()
+    for _ in range(steps):
+        rh.attn_bwd(q, k, v, out, lse, dy, w.frames, w.tokens_per_frame, Tc, To, phi, grads=grads)
+    e2.record()
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+    bwd_ms = e1.elapsed_time(e2) / steps
+    flops = 2.5 * cnt["softmax_flops"]
+    return {"fwd_lse_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "train_tokens_per_s": round(w.tokens / ((fwd_ms + bwd_ms) / 1000.0), 1),
+            "bwd_tflops": round(flops / (bwd_ms / 1000.0) / 1e12, 2), "bwd_algorithmic_flops": flops,
+            "bwd_frac": round(flops / (bwd_ms / 1000.0) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def length_scaling_bench(rh, hip, inputs, warmup):
     """Forward time against clip length: the first F = 21, 42, ..., 105 latent
     frames (1560 tokens each) of the 105-frame workload, T_c = 3, T_o = 1,
@@ -281,6 +314,7 @@ def main():
     ap.add_argument("--no-bidir", action="store_true")
     ap.add_argument("--no-learned", action="store_true")
     ap.add_argument("--no-length", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--learned-hidden", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -367,6 +401,10 @@ def main():
         learned = learned_map_bench(rh, hip, inputs, qg, kg, vg, out, w, Tc, To, args.learned_hidden,
                                     max(3, args.steps // 2), cnt)
 
+    backward = None
+    if not args.no_backward and phi in ("elu1", "poly2", "none"):
+        backward = backward_bench(rh, inputs, qg, kg, vg, w, Tc, To, phi, max(3, args.steps // 2), cnt)
+
     length = None
     if not args.no_length and w.name == "wan_21x30x52" and Tc == 3 and phi == "elu1":
         length = length_scaling_bench(rh, hip, inputs, args.warmup)
@@ -390,6 +428,7 @@ def main():
         "dense_softmax": dense,
         "bidirectional": bidir,
         "learned_map": learned,
+        "backward": backward,
         "length_scaling": length,
         "cpu_baseline": cpu,
     }

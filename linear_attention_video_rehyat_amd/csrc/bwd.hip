@@ -38,11 +38,21 @@ namespace rehyat {
 
 namespace {
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdKeys = 32 * kBwdWaves;   // keys per dk/dv workgroup
-constexpr int kBwdQRows = 64;              // query rows per dk/dv LDS tile
-constexpr int kBwdQueries = 32 * kBwdWaves;  // queries per dq workgroup
-constexpr int kBwdKTile = 64;              // keys per dq LDS tile
+#ifndef REHYAT_BWD_KWAVES
+#define REHYAT_BWD_KWAVES 4
+#endif
+#ifndef REHYAT_BWD_QWAVES
+#define REHYAT_BWD_QWAVES 8
+#endif
+#ifndef REHYAT_BWD_QROWS
+#define REHYAT_BWD_QROWS 64
+#endif
+constexpr int kBwdKWaves = REHYAT_BWD_KWAVES;  // waves of a dk/dv workgroup (32 keys each)
+constexpr int kBwdQWaves = REHYAT_BWD_QWAVES;  // waves of a dq workgroup (32 queries each)
+constexpr int kBwdKeys = 32 * kBwdKWaves;      // keys per dk/dv workgroup
+constexpr int kBwdQRows = REHYAT_BWD_QROWS;    // query rows per dk/dv LDS tile
+constexpr int kBwdQueries = 32 * kBwdQWaves;   // queries per dq workgroup
+constexpr int kBwdKTile = 64;                  // keys per dq LDS tile
 
 // elu(x) + 1 and its derivative
 __device__ __forceinline__ float elu1_grad(float x) { return x > 0.0f ? 1.0f : __expf(x); }
@@ -100,8 +110,8 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
 
 // ------------------------------------------------------------------ dk / dv (bf16)
 template <int D, int PHI>
-__global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) {
-    constexpr int NW = kBwdWaves, BQ = kBwdQRows;
+__global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p) {
+    constexpr int NW = kBwdKWaves, BQ = kBwdQRows;
     constexpr int C = D / 8, KS = D / 16, DT = D / 32;
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     constexpr int KSL = DP / 16, FT = DP / 32;
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
     constexpr int OPW = 2 * NI / NW;                   // per wave, Q and dY
     static_assert(2 * NI % NW == 0, "tile loads must split evenly");
     __shared__ __attribute__((aligned(16))) uint16_t tiles_raw[2][2 * QT];
-    __shared__ __attribute__((aligned(16))) float rowf[2][2][BQ];   // lse, dsum
+    __shared__ __attribute__((aligned(16))) float rowf[2][2][BQ];   // lse log2(e), dsum
     __shared__ __attribute__((aligned(16))) int roww[2][2][BQ];     // window bounds
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -165,13 +175,16 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
                                                      16, off, 0, 0, 0);
         }
     };
-    // per-row data of a tile: wave 0 loads it into registers, stores it later
+    // per-row data of a tile: waves 0 .. BQ/64-1 load it into registers (one
+    // row per lane) and store it after the current tile
+    static_assert(BQ % 64 == 0 && BQ / 64 <= NW, "row data: one row per lane of the first waves");
+    constexpr int RW = BQ / 64;
     float rl = 0.0f, rd = 0.0f;
     int rw0 = 0, rw1 = 0;
     auto fetch_rows = [&](int it) {
-        const int i = qr0 + it * BQ + lane;
+        const int i = qr0 + it * BQ + 64 * wave + lane;
         if (i < qr1) {
-            rl = lseb[i];
+            rl = lseb[i] * kLog2e;
             rd = dsb[i];
             row_window(p, i, rw0, rw1);
         } else {
@@ -180,10 +193,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
         }
     };
     auto store_rows = [&](int buf) {
-        rowf[buf][0][lane] = rl;
-        rowf[buf][1][lane] = rd;
-        roww[buf][0][lane] = rw0;
-        roww[buf][1][lane] = rw1;
+        rowf[buf][0][64 * wave + lane] = rl;
+        rowf[buf][1][64 * wave + lane] = rd;
+        roww[buf][0][64 * wave + lane] = rw0;
+        roww[buf][1][64 * wave + lane] = rw1;
     };
 
     // transposing-read offsets (dY^T / Q^T fragments: lane row d = 32 c + lq,
@@ -206,74 +219,8 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
         dkt[dt] = f32x16{};
     }
 
-    if (ntiles > 0) {
-        load_tile(0, 0);
-        if (wave == 0) {
-            fetch_rows(0);
-            store_rows(0);
-        }
-    }
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-        lds_barrier();
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            load_tile(buf ^ 1, it + 1);
-            if (wave == 0) fetch_rows(it + 1);
-        }
-        const lds_u16* Qs = (const lds_u16*)tiles_raw[buf];
-        const lds_u16* Ys = Qs + QT;
-#pragma unroll
-        for (int qs = 0; qs < BQ / 32; ++qs) {
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-            const int arow = 32 * qs + lq;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
-                sacc = mfma32x32x16(lds_read_b128(Qs, off), kf[s], sacc);
-                pacc = mfma32x32x16(lds_read_b128(Ys, off), vf[s], pacc);
-            }
-            // rows 32 qs + 8 j + 4 h + i of the tile, column = the lane's key
-            u32x4 pw[2], dw[2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r0 = 32 * qs + 8 * j + 4 * h;
-                const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][0][r0];
-                const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][1][r0];
-                float pv[4], dv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int w0 = roww[buf][0][r0 + i], w1 = roww[buf][1][r0 + i];
-                    const bool in = key_ok && key >= w0 && key < w1;
-                    const float pe = in ? __builtin_amdgcn_exp2f((sacc[4 * j + i] - l4[i]) * kLog2e) : 0.0f;
-                    pv[i] = pe;
-                    dv[i] = pe * (pacc[4 * j + i] - d4[i]);
-                }
-                pw[j >> 1][2 * (j & 1)] = pack2_bf16(pv[0], pv[1]);
-                pw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(pv[2], pv[3]);
-                dw[j >> 1][2 * (j & 1)] = pack2_bf16(dv[0], dv[1]);
-                dw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(dv[2], dv[3]);
-            }
-            // dV^T += dY^T P, dK^T += Q^T dS over the subtile's 32 queries (two 16-row steps)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int r16 = (32 * qs + 16 * kk) * D;
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
-                const bf16x8 db = __builtin_bit_cast(bf16x8, dw[kk]);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const bf16x8 ya = cat(lds_read_tr(Ys, r16 + toff[dt][0]), lds_read_tr(Ys, r16 + toff[dt][1]));
-                    const bf16x8 qa = cat(lds_read_tr(Qs, r16 + toff[dt][0]), lds_read_tr(Qs, r16 + toff[dt][1]));
-                    dvt[dt] = mfma32x32x16(ya, pb, dvt[dt]);
-                    dkt[dt] = mfma32x32x16(qa, db, dkt[dt]);
-                }
-            }
-        }
-        if (more && wave == 0) store_rows(buf ^ 1);
-    }
-
-    // ---- linear branch of the wave's keys (delta blocks u <= C-2)
+    // ---- linear branch of the wave's keys (delta blocks u <= C-2), first: its
+    // temporaries are dead before the main loop needs its registers
     if constexpr (PHI != kPhiNone) {
         if (p.lin) {
             const int u_key = (keyc / p.HW + p.To) / p.Tc;
@@ -287,8 +234,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
                 const uint16_t* gthi = (const uint16_t*)p.gt_hi + sofs;
                 const uint16_t* gtlo = (const uint16_t*)p.gt_lo + sofs;
                 const float* gz = p.gz + (long long)bh * p.C * p.z_stride + (long long)u * p.z_stride;
-                // dv += G_u^T phi(k): A = G_u^T rows (d), B = phi(k) (masked to the block's keys)
-#pragma unroll
+                // dv += G_u^T phi(k): A = G_u^T rows (d), B = phi(k) (masked to the block's keys);
+                // one output tile at a time (unrolled, the loads of every tile would be
+                // hoisted and held in registers)
+#pragma unroll 1
                 for (int dt = 0; dt < DT; ++dt) {
                     f32x16 acc = f32x16{};
 #pragma unroll
@@ -312,10 +261,12 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
                         acc = mfma32x32x16(al, fh, acc);
                         acc = mfma32x32x16(ah, fl, acc);
                     }
-                    dvt[dt] += acc;
+#pragma unroll
+                    for (int x = 0; x < DT; ++x)  // static register indices (dt is not unrolled)
+                        if (x == dt) dvt[x] += acc;
                 }
                 // dphi(k) = G_u v - g_u: A = G_u rows (features), B = V^T (the lane's key)
-#pragma unroll
+#pragma unroll 1
                 for (int ft = 0; ft < FT; ++ft) {
                     f32x16 acc = f32x16{};
 #pragma unroll
@@ -326,6 +277,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
                     }
                     if (!mine) continue;
                     const int dt = ft % DT;
+                    f32x16 add;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int f0 = 32 * ft + 8 * j + 4 * h;          // features f0 .. f0+3
@@ -334,12 +286,98 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
                         float kx[4];
                         load4_bf16(kbp + (long long)keyc * D + d0, kx);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            dkt[dt][4 * j + i] += feature_grad<D>(f0 + i, kx[i], acc[4 * j + i] - g4[i]);
+                        for (int i = 0; i < 4; ++i) add[4 * j + i] = feature_grad<D>(f0 + i, kx[i], acc[4 * j + i] - g4[i]);
                     }
+#pragma unroll
+                    for (int x = 0; x < DT; ++x)
+                        if (x == dt) dkt[x] += add;
                 }
             }
         }
+    }
+
+    if (ntiles > 0) {
+        load_tile(0, 0);
+        if (wave < RW) {
+            fetch_rows(0);
+            store_rows(0);
+        }
+    }
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        lds_barrier();
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            load_tile(buf ^ 1, it + 1);
+            if (wave < RW) fetch_rows(it + 1);
+        }
+        const lds_u16* Qs = (const lds_u16*)tiles_raw[buf];
+        const lds_u16* Ys = Qs + QT;
+        // every key of the block lies in the window of every row of the tile
+        // (windows move forward with the row): no masking needed
+        bool full;
+        {
+            const int ia = qr0 + it * BQ, ib = ia + BQ - 1;
+            int a0, a1, b0, b1;
+            row_window(p, ia, a0, a1);
+            row_window(p, ib, b0, b1);
+            full = ib < qr1 && kb0 + kBwdKeys <= p.N && b0 <= kb0 && a1 >= kb0 + kBwdKeys;
+        }
+#pragma unroll
+        for (int qs = 0; qs < BQ / 32; ++qs) {
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
+            const int arow = 32 * qs + lq;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
+                sacc = mfma32x32x16(lds_read_b128(Qs, off), kf[s], sacc);
+                pacc = mfma32x32x16(lds_read_b128(Ys, off), vf[s], pacc);
+            }
+            // rows 32 qs + 8 j + 4 h + i of the tile, column = the lane's key
+            u32x4 pw[2], dw[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = 32 * qs + 8 * j + 4 * h;
+                const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][0][r0];
+                const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][1][r0];
+                float pv[4], dv[4];
+                if (full) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - l4[i]);
+                } else {
+                    typedef int i32x4 __attribute__((ext_vector_type(4)));
+                    const i32x4 a4 = *(const __attribute__((address_space(3))) i32x4*)&roww[buf][0][r0];
+                    const i32x4 b4 = *(const __attribute__((address_space(3))) i32x4*)&roww[buf][1][r0];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool in = key_ok && key >= a4[i] && key < b4[i];
+                        pv[i] = in ? __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - l4[i]) : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dv[i] = pv[i] * (pacc[4 * j + i] - d4[i]);
+                pw[j >> 1][2 * (j & 1)] = pack2_bf16(pv[0], pv[1]);
+                pw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(pv[2], pv[3]);
+                dw[j >> 1][2 * (j & 1)] = pack2_bf16(dv[0], dv[1]);
+                dw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(dv[2], dv[3]);
+            }
+            // dV^T += dY^T P, dK^T += Q^T dS over the subtile's 32 queries (two 16-row steps)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r16 = (32 * qs + 16 * kk) * D;
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
+                const bf16x8 db = __builtin_bit_cast(bf16x8, dw[kk]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x8 ya = cat(lds_read_tr(Ys, r16 + toff[dt][0]), lds_read_tr(Ys, r16 + toff[dt][1]));
+                    const bf16x8 qa = cat(lds_read_tr(Qs, r16 + toff[dt][0]), lds_read_tr(Qs, r16 + toff[dt][1]));
+                    dvt[dt] = mfma32x32x16(ya, pb, dvt[dt]);
+                    dkt[dt] = mfma32x32x16(qa, db, dkt[dt]);
+                }
+            }
+        }
+        if (more && wave < RW) store_rows(buf ^ 1);
     }
 
     if (!key_ok) return;
@@ -359,8 +397,8 @@ __global__ __launch_bounds__(kBwdWaves * 64) void dkdv_bf16_kernel(BwdParams p) 
 
 // ------------------------------------------------------------------ dq (bf16)
 template <int D, int PHI>
-__global__ __launch_bounds__(kBwdWaves * 64) void dq_bf16_kernel(BwdParams p, int tiles_per_chunk) {
-    constexpr int NW = kBwdWaves, BN = kBwdKTile;
+__global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, int tiles_per_chunk) {
+    constexpr int NW = kBwdQWaves, BN = kBwdKTile;
     constexpr int C = D / 8, KS = D / 16, DT = D / 32;
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     constexpr int FT = DP / 32;
@@ -706,8 +744,8 @@ hipError_t launch_bf16_dp(const BwdParams& p, hipStream_t s) {
     const long long kblocks = (long long)p.BH * ((p.N + kBwdKeys - 1) / kBwdKeys);
     const int tpc = dq_tiles_per_chunk(p, kBwdQueries);
     const long long qblocks = (long long)p.BH * p.C * tpc;
-    if (kblocks > 0) dkdv_bf16_kernel<D, PHI><<<(unsigned)kblocks, kBwdWaves * 64, 0, s>>>(p);
-    if (qblocks > 0) dq_bf16_kernel<D, PHI><<<(unsigned)qblocks, kBwdWaves * 64, 0, s>>>(p, tpc);
+    if (kblocks > 0) dkdv_bf16_kernel<D, PHI><<<(unsigned)kblocks, kBwdKWaves * 64, 0, s>>>(p);
+    if (qblocks > 0) dq_bf16_kernel<D, PHI><<<(unsigned)qblocks, kBwdQWaves * 64, 0, s>>>(p, tpc);
     return hipGetLastError();
 }
 
