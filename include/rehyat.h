@@ -223,9 +223,11 @@ rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const v
 
 /*
  * Training direction (ReHyAt §3.4: attention distillation and fine-tuning
- * backpropagate through the hybrid attention), recurrent partition only.
+ * backpropagate through the hybrid attention).  causal != 0 selects the
+ * recurrent partition (rehyat_attn_fwd), causal == 0 the bidirectional one
+ * (rehyat_attn_fwd_bidir); the backward must use the forward's choice.
  *
- * rehyat_attn_fwd_lse: rehyat_attn_fwd (dtype REHYAT_BF16 or REHYAT_F32) that also
+ * rehyat_attn_fwd_lse: the forward (dtype REHYAT_BF16 or REHYAT_F32) that also
  *   writes lse [B][H][N] fp32 = ln(n^S + n^L), the joint normaliser of each query.
  * rehyat_attn_bwd: gradients of sum(dout * out) with respect to q, k and v, given
  *   the forward's inputs, out and lse, and dout (same shape and dtype as out).
@@ -233,17 +235,19 @@ rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const v
  *   no input and no other gradient.  feature_map NONE, ELU1 or POLY2 (the learned
  *   map is not differentiated here).  The gradients of the linear branch flow
  *   through the same cached sums as the forward: the forward states S_t, z_t,
- *   and their reverse-order counterpart, suffix sums over later chunks of
- *   e^{-lse} phi(q) dout^T.  Workspace comes from the forward's per-device arena.
+ *   and their reverse-order counterpart, sums over the chunks whose linear set
+ *   holds a key's block (later chunks; bidirectional: later and earlier ones)
+ *   of e^{-lse} phi(q) dout^T.  Workspace comes from the forward's per-device arena.
  *   Deterministic: no atomics, fixed summation order.
  */
 rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int dtype,
                                   int B, int H, int frames, int tokens_per_frame, int head_dim,
-                                  int chunk_frames, int overlap_frames, int feature_map, void* stream);
+                                  int chunk_frames, int overlap_frames, int feature_map, int causal,
+                                  void* stream);
 rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                               const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H,
                               int frames, int tokens_per_frame, int head_dim, int chunk_frames,
-                              int overlap_frames, int feature_map, void* stream);
+                              int overlap_frames, int feature_map, int causal, void* stream);
 
 /*
  * Profiling aid.  While set on the calling thread, every whole-clip forward

@@ -94,9 +94,9 @@ def load_library():
     lib.rehyat_attn_fwd_mlp_partials.restype = i
     lib.rehyat_attn_step_mlp.argtypes = [ctypes.POINTER(_StepStateC), vp, vp, vp, vp, i, mp, mp, vp]
     lib.rehyat_attn_step_mlp.restype = i
-    lib.rehyat_attn_fwd_lse.argtypes = [vp] * 5 + [i] * 9 + [vp]
+    lib.rehyat_attn_fwd_lse.argtypes = [vp] * 5 + [i] * 10 + [vp]
     lib.rehyat_attn_fwd_lse.restype = i
-    lib.rehyat_attn_bwd.argtypes = [vp] * 9 + [i] * 9 + [vp]
+    lib.rehyat_attn_bwd.argtypes = [vp] * 9 + [i] * 10 + [vp]
     lib.rehyat_attn_bwd.restype = i
     lib.rehyat_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     lib.rehyat_set_profile_events.restype = i
@@ -267,9 +267,9 @@ def attn_fwd_partials(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_f
 
 
 def attn_fwd_lse(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, feature_map="elu1",
-                 out=None, lse=None, stream=None):
-    """Forward (recurrent partition) that also returns lse [B, H, N] fp32 =
-    ln(n^S + n^L) per query, the normaliser the backward needs: (out, lse)."""
+                 out=None, lse=None, stream=None, causal=True):
+    """Forward that also returns lse [B, H, N] fp32 = ln(n^S + n^L) per query,
+    the normaliser the backward needs: (out, lse)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -280,14 +280,15 @@ def attn_fwd_lse(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     _check(lib.rehyat_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                    _dtype_id(q), B, H, frames, tokens_per_frame, d, chunk_frames,
-                                   overlap_frames, feature_map_id(feature_map), _stream_handle(stream)))
+                                   overlap_frames, feature_map_id(feature_map), 1 if causal else 0,
+                                   _stream_handle(stream)))
     return out, lse
 
 
 def attn_bwd(q, k, v, out, lse, dout, frames, tokens_per_frame, chunk_frames, overlap_frames,
-             feature_map="elu1", grads=None, stream=None):
-    """Gradients (dq, dk, dv) of sum(dout * out) for the recurrent hybrid
-    attention, given the forward's inputs, out and lse (attn_fwd_lse)."""
+             feature_map="elu1", grads=None, stream=None, causal=True):
+    """Gradients (dq, dk, dv) of sum(dout * out) for the hybrid attention (the
+    forward's partition), given its inputs, out and lse (attn_fwd_lse)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -301,7 +302,7 @@ def attn_bwd(q, k, v, out, lse, dout, frames, tokens_per_frame, chunk_frames, ov
     _check(lib.rehyat_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _dtype_id(q),
                                B, H, frames, tokens_per_frame, d, chunk_frames, overlap_frames,
-                               feature_map_id(feature_map), _stream_handle(stream)))
+                               feature_map_id(feature_map), 1 if causal else 0, _stream_handle(stream)))
     return dq, dk, dv
 
 

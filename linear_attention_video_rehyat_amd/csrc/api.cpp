@@ -435,46 +435,52 @@ rehyat_status partials_entry(const void* q, const void* k, const void* v, int dt
 
 // ---------------------------------------------------------------- backward
 // Workspace of the backward: dsum, the forward's prepared states (both
-// layouts), and the gradient sums per chunk-row block with their suffixes.
+// layouts), and the gradient sums per chunk-row block with their suffix (or,
+// bidirectional, prefix + suffix) combinations per key block.
 struct BwdWorkspace {
-    size_t dsum_off, part_off, shi_off, slo_off, thi_off, tlo_off, z_off;
-    size_t gpart_off, ghi_off, glo_off, gthi_off, gtlo_off, gz_off, total;
-    int n_sub, gn_sub;
+    size_t dsum_off, part_off, shi_off, slo_off, thi_off, tlo_off, z_off, suffix_off;
+    size_t gpart_off, ghi_off, glo_off, gthi_off, gtlo_off, gz_off, gsuffix_off, total;
+    int U, GU, gslots;
     SubSplit split, gsplit;
 };
 
-BwdWorkspace bwd_workspace(const Geometry& g) {
+BwdWorkspace bwd_workspace(const Geometry& g, int mode) {
     BwdWorkspace w{};
     const bool bf = g.dtype == REHYAT_BF16;
-    w.split = state_split(g.dtype, (long long)g.Tc * g.HW);   // delta blocks: at most T_c frames
-    w.gsplit = w.split;                                        // chunk-row blocks: at most T_c frames
-    w.n_sub = w.split.n_sub;
-    w.gn_sub = w.gsplit.n_sub;
-    const int U = std::max(g.C - 1, 0);
+    const bool bidir = mode == kBidirectional;
+    w.U = state_block_count(mode, g.C);                          // forward blocks
+    w.GU = bidir ? g.C : std::max(g.C - 1, 0);                   // chunk-row blocks
+    w.gslots = bidir ? 2 * g.C + 1 : g.C;                        // gradient sums per key block
+    long long block_frames = g.Tc;
+    if (bidir && g.To % g.Tc != 0) block_frames = std::max(g.To % g.Tc, g.Tc - g.To % g.Tc);
+    w.split = state_split(g.dtype, block_frames * g.HW);
+    w.gsplit = state_split(g.dtype, (long long)g.Tc * g.HW);    // a chunk: at most T_c frames
     const size_t prep = (size_t)g.BH * g.C * g.d * g.Dp * (bf ? 2 : 4);
-    const size_t zs = (size_t)g.BH * g.C * g.Dp * 4;
+    const size_t gprep = (size_t)g.BH * w.gslots * g.d * g.Dp * (bf ? 2 : 4);
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
     w.dsum_off = take((size_t)g.BH * g.N * 4);
-    w.part_off = take((size_t)g.BH * U * w.n_sub * g.E * 4);
+    w.part_off = take((size_t)g.BH * w.U * w.split.n_sub * g.E * 4);
     w.shi_off = take(prep);
     w.slo_off = take(bf ? prep : 0);
     w.thi_off = take(prep);
     w.tlo_off = take(bf ? prep : 0);
-    w.z_off = take(zs);
-    w.gpart_off = take((size_t)g.BH * U * w.gn_sub * g.E * 4);
-    w.ghi_off = take(prep);
-    w.glo_off = take(bf ? prep : 0);
-    w.gthi_off = take(prep);
-    w.gtlo_off = take(bf ? prep : 0);
-    w.gz_off = take(zs);
+    w.z_off = take((size_t)g.BH * g.C * g.Dp * 4);
+    w.suffix_off = take(bidir ? (size_t)g.BH * g.C * g.E * 4 : 0);
+    w.gpart_off = take((size_t)g.BH * w.GU * w.gsplit.n_sub * g.E * 4);
+    w.ghi_off = take(gprep);
+    w.glo_off = take(bf ? gprep : 0);
+    w.gthi_off = take(gprep);
+    w.gtlo_off = take(bf ? gprep : 0);
+    w.gz_off = take((size_t)g.BH * w.gslots * g.Dp * 4);
+    w.gsuffix_off = take(bidir ? (size_t)g.BH * (g.C + 1) * g.E * 4 : 0);
     w.total = off;
     return w;
 }
 
 rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void* out, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H, int frames,
-                        int tpf, int d, int Tc, int To, int phi, void* stream) {
+                        int tpf, int d, int Tc, int To, int phi, int mode, void* stream) {
     Geometry g{};
     rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
     if (st != REHYAT_OK) return st;
@@ -495,8 +501,9 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
     g_last_error.clear();
     hipStream_t s = (hipStream_t)stream;
     const bool bf = g.dtype == REHYAT_BF16;
-    const bool lin = any_linear(g, kCausal);
-    const BwdWorkspace w = bwd_workspace(g);
+    const bool bidir = mode == kBidirectional;
+    const bool lin = any_linear(g, mode);
+    const BwdWorkspace w = bwd_workspace(g, mode);
     void* wsp = nullptr;
     if ((st = arena_get(w.total, &wsp)) != REHYAT_OK) return st;
     char* ws = (char*)wsp;
@@ -507,17 +514,16 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
     bp.dq = dq; bp.dk = dk; bp.dv = dv;
     bp.bh_stride = g.N * g.d;
     bp.N = (int)g.N; bp.HW = g.HW; bp.F = g.F; bp.Tc = g.Tc; bp.To = g.To; bp.C = g.C; bp.BH = g.BH;
-    bp.d = g.d; bp.phi = lin ? g.phi : REHYAT_PHI_NONE; bp.lin = lin ? 1 : 0;
+    bp.d = g.d; bp.phi = lin ? g.phi : REHYAT_PHI_NONE; bp.lin = lin ? 1 : 0; bp.mode = mode;
     hipError_t e = launch_bwd_dsum(bp, (float*)(ws + w.dsum_off), bf, s);
     if (e != hipSuccess) return hip_fail(e, "backward dsum launch");
     if (lin) {
-        const int U = g.C - 1;
         // the forward's states S_t, z_t (both layouts of S_t)
         StateParams sp{};
         sp.k = k; sp.v = v; sp.bh_stride = g.N * g.d;
         sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
-        sp.n_blocks = U; sp.sub_rows = w.split.sub_rows; sp.n_sub = w.n_sub;
-        sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi; sp.mode = kCausal; sp.F = g.F;
+        sp.n_blocks = w.U; sp.sub_rows = w.split.sub_rows; sp.n_sub = w.split.n_sub;
+        sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi; sp.mode = mode; sp.F = g.F;
         sp.partial = (float*)(ws + w.part_off);
         e = bf ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
@@ -527,22 +533,25 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         cp.z = (float*)(ws + w.z_off);
         cp.s_chunk_stride = (long long)g.d * g.Dp; cp.s_bh_stride = (long long)g.C * g.d * g.Dp;
         cp.z_chunk_stride = g.Dp; cp.z_bh_stride = (long long)g.C * g.Dp;
-        cp.U = U; cp.n_sub = w.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
-        cp.t_first = 1; cp.t_offset = 0; cp.f32_prep = !bf; cp.mode = kCausal; cp.C = g.C;
+        cp.U = w.U; cp.n_sub = w.split.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
+        cp.t_first = bidir ? 0 : 1; cp.t_offset = 0; cp.f32_prep = !bf; cp.mode = mode; cp.C = g.C;
+        cp.q = g.To / g.Tc; cp.suffix = bidir ? (float*)(ws + w.suffix_off) : nullptr;
         if ((e = launch_scan(cp, s)) != hipSuccess) return hip_fail(e, "scan launch");
         // gradient sums per chunk (rows: the chunk's queries, second operand dy)
         StateParams gp = sp;
-        gp.k = q; gp.v = dout; gp.mode = kChunkRows;
-        gp.sub_rows = w.gsplit.sub_rows; gp.n_sub = w.gn_sub;
+        gp.k = q; gp.v = dout; gp.mode = bidir ? kChunkRowsAll : kChunkRows;
+        gp.n_blocks = w.GU; gp.sub_rows = w.gsplit.sub_rows; gp.n_sub = w.gsplit.n_sub;
         gp.row_lse = lse; gp.row_d = bp.dsum;
         gp.partial = (float*)(ws + w.gpart_off);
         e = bf ? launch_state_bf16(gp, s) : launch_state_f32(gp, s);
         if (e != hipSuccess) return hip_fail(e, "gradient-state launch");
         ScanParams gc = cp;
-        gc.partial = gp.partial; gc.n_sub = w.gn_sub;
+        gc.partial = gp.partial; gc.U = w.GU; gc.n_sub = w.gsplit.n_sub;
         gc.s_hi = ws + w.ghi_off; gc.s_lo = ws + w.glo_off; gc.t_hi = ws + w.gthi_off; gc.t_lo = ws + w.gtlo_off;
         gc.z = (float*)(ws + w.gz_off);
-        gc.t_first = 0; gc.mode = kChunkRows;
+        gc.s_bh_stride = (long long)w.gslots * g.d * g.Dp; gc.z_bh_stride = (long long)w.gslots * g.Dp;
+        gc.t_first = 0; gc.mode = bidir ? kBidirGrad : kChunkRows;
+        gc.suffix = bidir ? (float*)(ws + w.gsuffix_off) : nullptr;
         if ((e = launch_scan(gc, s)) != hipSuccess) return hip_fail(e, "gradient scan launch");
         bp.st_hi = ws + w.thi_off; bp.st_lo = ws + w.tlo_off; bp.z = (const float*)(ws + w.z_off);
         bp.g_hi = ws + w.ghi_off; bp.g_lo = ws + w.glo_off;
@@ -834,7 +843,7 @@ rehyat_status rehyat_attn_fwd_mlp_partials(const void* q, const void* k, const v
 
 rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int dtype,
                                   int B, int H, int frames, int tokens_per_frame, int head_dim, int chunk_frames,
-                                  int overlap_frames, int feature_map, void* stream) {
+                                  int overlap_frames, int feature_map, int causal, void* stream) {
     Geometry g{};
     rehyat_status st = check_common(g, B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
                                     feature_map, dtype);
@@ -848,16 +857,16 @@ rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, v
         overlaps(lse, lbytes, v, bytes))
         return fail(REHYAT_EINVAL, "out and lse must not overlap q, k, v or each other");
     g_last_error.clear();
-    return run_fwd(q, k, v, out, g, kCausal, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream,
-                   nullptr, nullptr, lse);
+    return run_fwd(q, k, v, out, g, causal ? kCausal : kBidirectional, nullptr, nullptr, nullptr, nullptr,
+                   nullptr, (hipStream_t)stream, nullptr, nullptr, lse);
 }
 
 rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                               const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H, int frames,
                               int tokens_per_frame, int head_dim, int chunk_frames, int overlap_frames,
-                              int feature_map, void* stream) {
+                              int feature_map, int causal, void* stream) {
     return bwd_entry(q, k, v, out, lse, dout, dq, dk, dv, dtype, B, H, frames, tokens_per_frame, head_dim,
-                     chunk_frames, overlap_frames, feature_map, stream);
+                     chunk_frames, overlap_frames, feature_map, causal ? kCausal : kBidirectional, stream);
 }
 
 rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int H, int rows, int head_dim,

@@ -223,17 +223,22 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
     // temporaries are dead before the main loop needs its registers
     if constexpr (PHI != kPhiNone) {
         if (p.lin) {
-            const int u_key = (keyc / p.HW + p.To) / p.Tc;
+            // block of the key: delta block E_u (recurrent form; u <= C-2 has a
+            // gradient sum) or bidirectional block b (2C+1 of them)
+            const bool bidir = p.mode == kBidirectional;
+            const int u_key = bidir ? bidir_block_of_frame(keyc / p.HW, p.Tc, p.To) : (keyc / p.HW + p.To) / p.Tc;
             const int u_first = __builtin_amdgcn_readfirstlane(u_key);
             const int u_last = __shfl(u_key, 31);
-            for (int u = u_first; u <= u_last && u <= p.C - 2; ++u) {
+            const int u_max = bidir ? 2 * p.C : p.C - 2;
+            const int slots = bidir ? 2 * p.C + 1 : p.C;
+            for (int u = u_first; u <= u_last && u <= u_max; ++u) {
                 const bool mine = key_ok && u_key == u;
-                const long long sofs = (long long)bh * p.C * p.s_stride + (long long)u * p.s_stride;
+                const long long sofs = (long long)bh * slots * p.s_stride + (long long)u * p.s_stride;
                 const uint16_t* ghi = (const uint16_t*)p.g_hi + sofs;
                 const uint16_t* glo = (const uint16_t*)p.g_lo + sofs;
                 const uint16_t* gthi = (const uint16_t*)p.gt_hi + sofs;
                 const uint16_t* gtlo = (const uint16_t*)p.gt_lo + sofs;
-                const float* gz = p.gz + (long long)bh * p.C * p.z_stride + (long long)u * p.z_stride;
+                const float* gz = p.gz + (long long)bh * slots * p.z_stride + (long long)u * p.z_stride;
                 // dv += G_u^T phi(k): A = G_u^T rows (d), B = phi(k) (masked to the block's keys);
                 // one output tile at a time (unrolled, the loads of every tile would be
                 // hoisted and held in registers)
@@ -522,7 +527,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
 
     // ---- linear branch: dphi(q) = e^{-lse} (S_t dy - D z_t)
     if constexpr (PHI != kPhiNone) {
-        if (p.lin && t * p.Tc - p.To > 0) {
+        if (p.lin && (p.mode == kBidirectional || t * p.Tc - p.To > 0)) {
             const long long sofs = (long long)bh * p.C * p.s_stride + (long long)t * p.s_stride;
             const uint16_t* sthi = (const uint16_t*)p.st_hi + sofs;
             const uint16_t* stlo = (const uint16_t*)p.st_lo + sofs;
@@ -636,11 +641,13 @@ __global__ __launch_bounds__(kF32Lanes) void dkdv_f32_kernel(BwdParams p) {
     }
     if (!key_ok) return;
     if (PHI != kPhiNone && p.lin) {
-        const int u = (key / p.HW + p.To) / p.Tc;
-        if (u <= p.C - 2) {
-            const long long sofs = (long long)bh * p.C * p.s_stride + (long long)u * p.s_stride;
+        const bool bidir = p.mode == kBidirectional;
+        const int u = bidir ? bidir_block_of_frame(key / p.HW, p.Tc, p.To) : (key / p.HW + p.To) / p.Tc;
+        const int slots = bidir ? 2 * p.C + 1 : p.C;
+        if (bidir || u <= p.C - 2) {
+            const long long sofs = (long long)bh * slots * p.s_stride + (long long)u * p.s_stride;
             const float* G = (const float*)p.gt_hi + sofs;   // [D'][d]
-            const float* gz = p.gz + (long long)bh * p.C * p.z_stride + (long long)u * p.z_stride;
+            const float* gz = p.gz + (long long)bh * slots * p.z_stride + (long long)u * p.z_stride;
             for (int f = 0; f < DP; ++f) {
                 const float x = k[f % D];
                 const float phi = f < D ? elu1(x) : x * x;
@@ -717,7 +724,7 @@ __global__ __launch_bounds__(kF32Lanes) void dq_f32_kernel(BwdParams p, int tile
         }
     }
     if (!row_ok) return;
-    if (PHI != kPhiNone && p.lin && t * p.Tc - p.To > 0) {
+    if (PHI != kPhiNone && p.lin && (p.mode == kBidirectional || t * p.Tc - p.To > 0)) {
         const long long sofs = (long long)bh * p.C * p.s_stride + (long long)t * p.s_stride;
         const float* S = (const float*)p.st_hi + sofs;   // [D'][d]
         const float* zt = p.z + (long long)bh * p.C * p.z_stride + (long long)t * p.z_stride;

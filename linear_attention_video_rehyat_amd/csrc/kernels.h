@@ -29,14 +29,27 @@ inline int feature_dim(int phi, int d) {
 //   max(2(t - q), 0) plus the blocks from 2t+3 on.
 //  kChunkRows (backward): block u = the frames of chunk u+1, u = 0 .. C-2
 //   (the queries whose gradient sums feed the keys of the earlier delta blocks).
-enum BlockMode { kCausal = 0, kBidirectional = 1, kChunkRows = 2 };
+//  kChunkRowsAll (backward of the bidirectional form): block u = chunk u.
+//  kBidirGrad (scan only): slot b = sum over the chunks whose linear set holds
+//   the bidirectional block b (see scan.hip).
+enum BlockMode { kCausal = 0, kBidirectional = 1, kChunkRows = 2, kChunkRowsAll = 3, kBidirGrad = 4 };
 
-__host__ __device__ inline int state_block_count(int mode, int C) { return mode == kBidirectional ? 2 * C + 1 : C - 1; }
+__host__ __device__ inline int state_block_count(int mode, int C) {
+    return mode == kBidirectional ? 2 * C + 1 : (mode == kChunkRowsAll ? C : C - 1);
+}
+
+// Bidirectional block of frame f: block 2c = [c T_c - r, c T_c), 2c+1 = [c T_c, (c+1) T_c - r).
+__host__ __device__ inline int bidir_block_of_frame(int f, int Tc, int To) {
+    const int r = To % Tc;
+    const int c = (f + r) / Tc;
+    return f < c * Tc ? 2 * c : 2 * c + 1;
+}
 
 __host__ __device__ inline void state_block_frames(int mode, int u, int Tc, int To, int F, int& f0, int& f1) {
-    if (mode == kChunkRows) {
-        f0 = (u + 1) * Tc < F ? (u + 1) * Tc : F;
-        f1 = (u + 2) * Tc < F ? (u + 2) * Tc : F;
+    if (mode == kChunkRows || mode == kChunkRowsAll) {
+        const int c = mode == kChunkRows ? u + 1 : u;
+        f0 = c * Tc < F ? c * Tc : F;
+        f1 = (c + 1) * Tc < F ? (c + 1) * Tc : F;
         return;
     }
     if (mode == kCausal) {
@@ -200,6 +213,8 @@ struct BwdParams {
     const void* g_hi; const void* g_lo; const void* gt_hi; const void* gt_lo; const float* gz;
     long long s_stride, z_stride;     // per chunk / per block: d*D' and D' elements (bh stride = C times)
     int lin;                          // the linear branch is active (some chunk has a linear set)
+    int mode;                         // kCausal or kBidirectional (then: G per bidirectional block,
+                                      // 2C+1 slots, and every chunk has a linear set)
 };
 
 // Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot

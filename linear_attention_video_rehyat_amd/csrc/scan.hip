@@ -79,6 +79,30 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
         }
         return;
     }
+    if (p.mode == kBidirGrad) {
+        // blocks = chunks 0 .. C-1 (U = C).  Bidirectional block b lies in the
+        // linear set of chunk t iff b < 2(t - q) or b >= 2t + 3, i.e. for
+        // t >= q + b/2 + 1 (suffix over chunks) and t <= (b - 3)/2 (prefix).
+        // Suffix sums Y_t = sum_{t' >= t} into scratch (Y_C = 0), then slot b =
+        // prefix + Y[min(q + b/2 + 1, C)] for b = 0 .. 2C.
+        float* suf = p.suffix + (long long)bh * (p.C + 1) * E + e4;
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)(suf + (long long)p.C * E) = y;
+        for (int t = p.C - 1; t >= 0; --t) {
+            y += block_sum(t);
+            *(f32x4*)(suf + (long long)t * E) = y;
+        }
+        int pt = 0;  // chunks summed into the prefix x
+        for (int b = 0; b <= 2 * p.C; ++b) {
+            const int pe = b >= 3 ? (b - 3) / 2 + 1 : 0;  // prefix: chunks < pe
+            for (; pt < min(pe, p.C); ++pt) x += block_sum(pt);
+            const f32x4 keep = x;
+            x += *(const f32x4*)(suf + (long long)min(p.q + b / 2 + 1, p.C) * E);
+            emit(b);
+            x = keep;
+        }
+        return;
+    }
     if (p.mode == kBidirectional) {
         // suffix sums Y_k = sum of blocks k.. U-1, backwards; chunk t needs
         // Y_{2t+3} (zero past the last block).  Each thread keeps its own 4

@@ -2,8 +2,8 @@
 fp64 oracle.
 
 rehyat_attn_fwd_lse returns the output and lse = ln(n^S + n^L) per query;
-rehyat_attn_bwd returns dq, dk, dv of sum(dout * out) for the recurrent
-partition.  The oracle's gradients (oracle.backward) come from fp64 reverse
+rehyat_attn_bwd returns dq, dk, dv of sum(dout * out), for the recurrent
+(§3.3) and the bidirectional (§3.2 with overlap) partitions.  The oracle's gradients (oracle.backward) come from fp64 reverse
 mode of the matrix form and are pinned on the CPU by central differences of the
 definition form.  fp32 workloads: rel-L2 <= 1e-5 per gradient.  bf16 workloads:
 rel-L2 <= 1e-2 per gradient and max-abs <= 3e-2 of the largest reference entry
@@ -21,16 +21,16 @@ from tests.parity_util import gpu, rel_l2, sync, to64
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, phi, Tc=None, To=None):
+def _run(w, phi, Tc=None, To=None, causal=True):
     Tc = w.chunk_frames if Tc is None else Tc
     To = w.overlap_frames if To is None else To
     q, k, v = inputs.make_qkv(w)
     dy = inputs.make_dout(w)
     qg, kg, vg, dyg = gpu(q, k, v, dy)
-    out, lse = rh.attn_fwd_lse(qg, kg, vg, w.frames, w.tokens_per_frame, Tc, To, phi)
-    grads = rh.attn_bwd(qg, kg, vg, out, lse, dyg, w.frames, w.tokens_per_frame, Tc, To, phi)
+    out, lse = rh.attn_fwd_lse(qg, kg, vg, w.frames, w.tokens_per_frame, Tc, To, phi, causal=causal)
+    grads = rh.attn_bwd(qg, kg, vg, out, lse, dyg, w.frames, w.tokens_per_frame, Tc, To, phi, causal=causal)
     sync()
-    ref = O.backward(to64(q), to64(k), to64(v), to64(dy), w.tokens_per_frame, Tc, To, phi)
+    ref = O.backward(to64(q), to64(k), to64(v), to64(dy), w.tokens_per_frame, Tc, To, phi, causal=causal)
     return (q, k, v, dy), out, lse, grads, ref, Tc, To
 
 
@@ -42,19 +42,21 @@ def _check(grads, ref, tol_rel, tol_abs, what):
         assert e <= tol_rel and a <= tol_abs, f"{what} {name}: rel-L2 {e:.3e}, max-abs/scale {a:.3e}"
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("phi", ["elu1", "poly2", "none"])
-def test_tiny_f32(phi):
+def test_tiny_f32(phi, causal):
     w = inputs.WORKLOADS["tiny_f4x8x8"]
-    _, _, _, grads, ref, _, _ = _run(w, phi)
-    _check(grads, ref, 1e-5, 1e-4, f"tiny fp32 {phi}")
+    _, _, _, grads, ref, _, _ = _run(w, phi, causal=causal)
+    _check(grads, ref, 1e-5, 1e-4, f"tiny fp32 {phi} causal={causal}")
 
 
-@pytest.mark.parametrize("Tc,To", [(1, 0), (2, 1), (3, 4), (2, 2)])
-def test_f32_geometries(Tc, To):
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Tc,To", [(1, 0), (2, 1), (3, 4), (2, 2), (3, 5)])
+def test_f32_geometries(Tc, To, causal):
     w = inputs.custom(1, 2, 7, 23, 16, Tc, To, dtype="f32", seed_id=1100 + 10 * Tc + To)
     for phi in ("elu1", "poly2"):
-        _, _, _, grads, ref, _, _ = _run(w, phi)
-        _check(grads, ref, 1e-5, 1e-4, f"fp32 Tc{Tc} To{To} {phi}")
+        _, _, _, grads, ref, _, _ = _run(w, phi, causal=causal)
+        _check(grads, ref, 1e-5, 1e-4, f"fp32 Tc{Tc} To{To} {phi} causal={causal}")
 
 
 SMALL = [
@@ -76,16 +78,28 @@ def test_bf16_small(geom, phi):
     _check(grads, ref, 1e-2, 3e-2, f"bf16 {geom} {phi}")
 
 
+@pytest.mark.parametrize("geom", SMALL + [(1, 1, 8, 50, 128, 2, 4), (1, 1, 9, 40, 64, 3, 5)],
+                         ids=lambda g: "B{}H{}F{}HW{}d{}Tc{}To{}".format(*g))
+@pytest.mark.parametrize("phi", ["elu1", "poly2"])
+def test_bf16_small_bidirectional(geom, phi):
+    B, H, F, HW, d, Tc, To = geom
+    w = inputs.custom(B, H, F, HW, d, Tc, To, dtype="bf16", seed_id=1250 + F * 7 + d)
+    _, _, _, grads, ref, _, _ = _run(w, phi, causal=False)
+    _check(grads, ref, 1e-2, 3e-2, f"bf16 bidirectional {geom} {phi}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_lse_matches_oracle(dtype):
+def test_lse_matches_oracle(dtype, causal):
     d = 16 if dtype == "f32" else 128
     w = inputs.custom(1, 2, 6, 50, d, 2, 1, dtype=dtype, seed_id=1300)
     q, k, v = inputs.make_qkv(w)
-    out, lse = rh.attn_fwd_lse(*gpu(q, k, v), w.frames, w.tokens_per_frame, 2, 1, "elu1")
-    y = rh.attn_fwd(*gpu(q, k, v), w.frames, w.tokens_per_frame, 2, 1, "elu1")
+    out, lse = rh.attn_fwd_lse(*gpu(q, k, v), w.frames, w.tokens_per_frame, 2, 1, "elu1", causal=causal)
+    y = rh.attn_fwd(*gpu(q, k, v), w.frames, w.tokens_per_frame, 2, 1, "elu1", causal=causal)
     sync()
     assert torch.equal(out, y)
-    _, parts = O.definition(to64(q), to64(k), to64(v), w.frames, w.tokens_per_frame, 2, 1, "elu1", partials=True)
+    _, parts = O.definition(to64(q), to64(k), to64(v), w.frames, w.tokens_per_frame, 2, 1, "elu1", partials=True,
+                            causal=causal)
     ref = np.log(np.exp(parts["m"]) * parts["nt"] + parts["nL"])
     np.testing.assert_allclose(to64(lse), ref, rtol=0, atol=1e-5 if dtype == "f32" else 2e-4)
 
