@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "7b74d4fb196f320e", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (256445 * 2.0 + 101472 * 1.0) * 1024}
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "bdd2934977fb5486", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (257913 * 2.0 + 101472 * 1.0) * 1024}
 
 
 LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h", "kernels.h")
@@ -181,6 +181,41 @@ def backward_bench(rh, inputs, q, k, v, w, Tc, To, phi, steps, cnt):
             "bwd_frac": round(flops / (bwd_ms / 1000.0) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def workload_sweep(rh, hip, inputs, steps):
+    """The other Wan-shaped workloads, one forward each: the CFG pair (B = 2)
+    with T_c = 1, 3, 7 next to dense softmax at that shape (local-window versus
+    linear-state cost), and the 21 x 45 x 80 clip with 1 % outlier keys."""
+    import torch
+    res = {}
+    wc = inputs.WORKLOADS["wan_cfg_21x30x52"]
+    q, k, v = (x.to("cuda") for x in inputs.make_qkv(wc))
+    out = torch.empty_like(q)
+    for Tc in (1, 3, 7):
+        t = time_steps(rh, hip, q, k, v, out, wc, Tc, 1, "elu1", steps, 1)
+        c = geometry_counts(wc, Tc, 1, wc.head_dim)
+        res[f"cfg_B2_Tc{Tc}"] = {
+            "ms_per_step": round(t["ms_per_step"], 4), "tokens_per_s": round(wc.tokens / (t["ms_per_step"] / 1000.0), 1),
+            "local_ms": round(t["local_ms"], 4), "local_tflops": round(c["softmax_flops"] / (t["local_ms"] / 1000.0) / 1e12, 2),
+            "state_pass_ms": round(t["state_ms"] + t["scan_ms"], 4),
+            "state_pass_gbs": round(c["state_bytes"] / ((t["state_ms"] + t["scan_ms"]) / 1000.0) / 1e9, 1)}
+    t = time_steps(rh, hip, q, k, v, out, wc, wc.frames, 0, "none", max(2, steps // 2), 1)
+    c = geometry_counts(wc, wc.frames, 0, 0)
+    res["cfg_B2_dense"] = {"ms_per_step": round(t["ms_per_step"], 4),
+                           "tokens_per_s": round(wc.tokens / (t["ms_per_step"] / 1000.0), 1),
+                           "tflops": round(c["softmax_flops"] / (t["local_ms"] / 1000.0) / 1e12, 2)}
+    del q, k, v, out
+    wo = inputs.WORKLOADS["wan_outlier_21x45x80"]
+    q, k, v = (x.to("cuda") for x in inputs.make_qkv(wo))
+    out = torch.empty_like(q)
+    t = time_steps(rh, hip, q, k, v, out, wo, wo.chunk_frames, wo.overlap_frames, "elu1", steps, 1)
+    c = geometry_counts(wo, wo.chunk_frames, wo.overlap_frames, wo.head_dim)
+    res["outlier_21x45x80"] = {
+        "ms_per_step": round(t["ms_per_step"], 4), "tokens_per_s": round(wo.tokens / (t["ms_per_step"] / 1000.0), 1),
+        "local_ms": round(t["local_ms"], 4), "local_tflops": round(c["softmax_flops"] / (t["local_ms"] / 1000.0) / 1e12, 2),
+        "state_pass_ms": round(t["state_ms"] + t["scan_ms"], 4)}
+    return res
+
+
 def length_scaling_bench(rh, hip, inputs, warmup):
     """Forward time against clip length: the first F = 21, 42, ..., 105 latent
     frames (1560 tokens each) of the 105-frame workload, T_c = 3, T_o = 1,
@@ -315,6 +350,7 @@ def main():
     ap.add_argument("--no-learned", action="store_true")
     ap.add_argument("--no-length", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--learned-hidden", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -405,6 +441,10 @@ def main():
     if not args.no_backward and phi in ("elu1", "poly2", "none"):
         backward = backward_bench(rh, inputs, qg, kg, vg, w, Tc, To, phi, max(3, args.steps // 2), cnt)
 
+    sweep = None
+    if not args.no_sweep and w.name == "wan_21x30x52" and phi == "elu1":
+        sweep = workload_sweep(rh, hip, inputs, max(3, args.steps // 4))
+
     length = None
     if not args.no_length and w.name == "wan_21x30x52" and Tc == 3 and phi == "elu1":
         length = length_scaling_bench(rh, hip, inputs, args.warmup)
@@ -430,6 +470,7 @@ def main():
         "learned_map": learned,
         "backward": backward,
         "length_scaling": length,
+        "other_workloads": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
