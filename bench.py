@@ -118,7 +118,10 @@ def geometry_counts(w, Tc, To, phi_dim):
             "bidir_state_bytes": bidir_bytes, "chunks": C}
 
 
-def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=True, causal=True):
+def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=True, causal=True, flush=None):
+    """Times `steps` forwards.  With `flush` (a device buffer), each step is
+    preceded by a write of the whole buffer, so that no input is left in the
+    last-level cache (only the per-kernel event times are meaningful then)."""
     import torch
     for _ in range(warmup):
         rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out, causal=causal)
@@ -129,6 +132,8 @@ def time_steps(rh, hip, q, k, v, out, w, Tc, To, phi, steps, warmup, profile=Tru
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 0xff)
         if profile:
             rh.set_profile_events(evs[i])
         rh.attn_fwd(q, k, v, w.frames, w.tokens_per_frame, Tc, To, phi, out=out, causal=causal)
@@ -406,6 +411,14 @@ def main():
         state = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(gbs / PEAK_HBM_GBS, 4), "state_kernel_ms": round(main_t["state_ms"], 4),
                  "scan_ms": round(main_t["scan_ms"], 4), "algorithmic_bytes": cnt["state_bytes"]}
+        # the same with the last-level cache flushed before every step (512 MB written)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ft = time_steps(rh, hip, qg, kg, vg, out, w, Tc, To, phi, max(5, args.steps // 2), 1, flush=scratch)
+        del scratch
+        fms = ft["state_ms"] + ft["scan_ms"]
+        state.update(flushed_state_kernel_ms=round(ft["state_ms"], 4), flushed_scan_ms=round(ft["scan_ms"], 4),
+                     flushed_achieved=round(cnt["state_bytes"] / (fms / 1000.0) / 1e9, 1),
+                     flushed_frac=round(cnt["state_bytes"] / (fms / 1000.0) / 1e9 / PEAK_HBM_GBS, 4))
 
     dense = None
     if not args.no_dense:

@@ -228,7 +228,14 @@ rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const v
  * (rehyat_attn_fwd_bidir); the backward must use the forward's choice.
  *
  * rehyat_attn_fwd_lse: the forward (dtype REHYAT_BF16 or REHYAT_F32) that also
- *   writes lse [B][H][N] fp32 = ln(n^S + n^L), the joint normaliser of each query.
+ *   writes lse [B][H][N] fp32 = ln(n^S + n^L), the joint normaliser of each query,
+ *   and, if out_f32 is not NULL (bf16 calls), the output before its rounding to
+ *   bf16, fp32 [B][H][N][head_dim].
+ * rehyat_attn_bwd uses out_f32 (may be NULL) rather than the bf16 out for the
+ *   row sums D = dout . out.  The linear sums of the bidirectional form cancel
+ *   in the gradient, which magnifies the bf16 rounding of out: there, dq drifts
+ *   to ~1e-2 relative error from the rounded out alone at the Wan shape (the
+ *   recurrent form: ~2e-4).
  * rehyat_attn_bwd: gradients of sum(dout * out) with respect to q, k and v, given
  *   the forward's inputs, out and lse, and dout (same shape and dtype as out).
  *   dq, dk, dv: caller-owned outputs in dtype, [B][H][N][head_dim], overlapping
@@ -240,13 +247,13 @@ rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const v
  *   of e^{-lse} phi(q) dout^T.  Workspace comes from the forward's per-device arena.
  *   Deterministic: no atomics, fixed summation order.
  */
-rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int dtype,
-                                  int B, int H, int frames, int tokens_per_frame, int head_dim,
-                                  int chunk_frames, int overlap_frames, int feature_map, int causal,
-                                  void* stream);
-rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                              const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H,
-                              int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  float* out_f32, int dtype, int B, int H, int frames, int tokens_per_frame,
+                                  int head_dim, int chunk_frames, int overlap_frames, int feature_map,
+                                  int causal, void* stream);
+rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* out_f32,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv, int dtype,
+                              int B, int H, int frames, int tokens_per_frame, int head_dim, int chunk_frames,
                               int overlap_frames, int feature_map, int causal, void* stream);
 
 /*

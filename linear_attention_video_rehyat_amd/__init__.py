@@ -94,9 +94,9 @@ def load_library():
     lib.rehyat_attn_fwd_mlp_partials.restype = i
     lib.rehyat_attn_step_mlp.argtypes = [ctypes.POINTER(_StepStateC), vp, vp, vp, vp, i, mp, mp, vp]
     lib.rehyat_attn_step_mlp.restype = i
-    lib.rehyat_attn_fwd_lse.argtypes = [vp] * 5 + [i] * 10 + [vp]
+    lib.rehyat_attn_fwd_lse.argtypes = [vp] * 6 + [i] * 10 + [vp]
     lib.rehyat_attn_fwd_lse.restype = i
-    lib.rehyat_attn_bwd.argtypes = [vp] * 9 + [i] * 10 + [vp]
+    lib.rehyat_attn_bwd.argtypes = [vp] * 10 + [i] * 10 + [vp]
     lib.rehyat_attn_bwd.restype = i
     lib.rehyat_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     lib.rehyat_set_profile_events.restype = i
@@ -267,9 +267,11 @@ def attn_fwd_partials(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_f
 
 
 def attn_fwd_lse(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, feature_map="elu1",
-                 out=None, lse=None, stream=None, causal=True):
+                 out=None, lse=None, stream=None, causal=True, out_f32=None):
     """Forward that also returns lse [B, H, N] fp32 = ln(n^S + n^L) per query,
-    the normaliser the backward needs: (out, lse)."""
+    the normaliser the backward needs: (out, lse).  out_f32=True (or a float32
+    tensor shaped like q) also keeps the bf16 call's output before rounding:
+    (out, lse, out_f32)."""
     torch = _torch()
     lib = load_library()
     _check_qkv(q, k, v)
@@ -278,15 +280,18 @@ def attn_fwd_lse(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    want32 = out_f32 is not None and out_f32 is not False
+    if out_f32 is True:
+        out_f32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _check(lib.rehyat_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                   _dtype_id(q), B, H, frames, tokens_per_frame, d, chunk_frames,
-                                   overlap_frames, feature_map_id(feature_map), 1 if causal else 0,
-                                   _stream_handle(stream)))
-    return out, lse
+                                   out_f32.data_ptr() if want32 else None, _dtype_id(q), B, H, frames,
+                                   tokens_per_frame, d, chunk_frames, overlap_frames, feature_map_id(feature_map),
+                                   1 if causal else 0, _stream_handle(stream)))
+    return (out, lse, out_f32) if want32 else (out, lse)
 
 
 def attn_bwd(q, k, v, out, lse, dout, frames, tokens_per_frame, chunk_frames, overlap_frames,
-             feature_map="elu1", grads=None, stream=None, causal=True):
+             feature_map="elu1", grads=None, stream=None, causal=True, out_f32=None):
     """Gradients (dq, dk, dv) of sum(dout * out) for the hybrid attention (the
     forward's partition), given its inputs, out and lse (attn_fwd_lse)."""
     torch = _torch()
@@ -299,7 +304,11 @@ def attn_bwd(q, k, v, out, lse, dout, frames, tokens_per_frame, chunk_frames, ov
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise RehyatError(1, "lse must be a contiguous float32 [B, H, N] tensor")
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
-    _check(lib.rehyat_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+    if out_f32 is not None and (out_f32.shape != q.shape or out_f32.dtype != torch.float32
+                                or not out_f32.is_contiguous()):
+        raise RehyatError(1, "out_f32 must be a contiguous float32 tensor shaped like q")
+    _check(lib.rehyat_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               out_f32.data_ptr() if out_f32 is not None else None, lse.data_ptr(),
                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _dtype_id(q),
                                B, H, frames, tokens_per_frame, d, chunk_frames, overlap_frames,
                                feature_map_id(feature_map), 1 if causal else 0, _stream_handle(stream)))

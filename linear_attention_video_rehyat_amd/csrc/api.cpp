@@ -298,7 +298,7 @@ void mlp_rows(const Geometry& g, int mode, int& q0, int& k1) {
 rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g, int mode,
                       float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s,
                       const rehyat_mlp_weights* wq = nullptr, const rehyat_mlp_weights* wk = nullptr,
-                      float* lse = nullptr) {
+                      float* lse = nullptr, float* out_f32 = nullptr) {
     const bool lin = any_linear(g, mode);
     char* ws = nullptr;
     FwdWorkspace w{};
@@ -373,6 +373,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
     }
     lp.pm = pm; lp.pnt = pnt; lp.poS = poS; lp.poL = poL; lp.pnL = pnL;
     lp.lse = lse;
+    lp.out_f32 = g.dtype == REHYAT_BF16 ? out_f32 : nullptr;
     hipError_t e = g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s);
     if (e != hipSuccess) return hip_fail(e, "local-attention launch");
     if ((e = prof_mark(3, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -478,9 +479,9 @@ BwdWorkspace bwd_workspace(const Geometry& g, int mode) {
     return w;
 }
 
-rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                        const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H, int frames,
-                        int tpf, int d, int Tc, int To, int phi, int mode, void* stream) {
+rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void* out, const float* out_f32,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int dtype, int B,
+                        int H, int frames, int tpf, int d, int Tc, int To, int phi, int mode, void* stream) {
     Geometry g{};
     rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype);
     if (st != REHYAT_OK) return st;
@@ -491,10 +492,13 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
     for (void* x : outs)
         if (!x || !aligned16(x)) return fail(REHYAT_EINVAL, "null or misaligned gradient pointer");
     const size_t bytes = (size_t)g.BH * g.N * g.d * g.elem;
+    if (out_f32 && !aligned16(out_f32)) return fail(REHYAT_EINVAL, "misaligned out_f32");
     for (int a = 0; a < 3; ++a) {
         for (int b = 0; b < 6; ++b)
             if (overlaps(outs[a], bytes, ins[b], b == 4 ? (size_t)g.BH * g.N * 4 : bytes))
                 return fail(REHYAT_EINVAL, "gradients must not overlap the inputs");
+        if (out_f32 && overlaps(outs[a], bytes, out_f32, (size_t)g.BH * g.N * g.d * 4))
+            return fail(REHYAT_EINVAL, "gradients must not overlap the inputs");
         for (int b = a + 1; b < 3; ++b)
             if (overlaps(outs[a], bytes, outs[b], bytes)) return fail(REHYAT_EINVAL, "gradients must not overlap");
     }
@@ -509,7 +513,7 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
     char* ws = (char*)wsp;
 
     BwdParams bp{};
-    bp.q = q; bp.k = k; bp.v = v; bp.dy = dout; bp.out = out;
+    bp.q = q; bp.k = k; bp.v = v; bp.dy = dout; bp.out = out; bp.out_f32 = bf ? out_f32 : nullptr;
     bp.lse = lse; bp.dsum = (const float*)(ws + w.dsum_off);
     bp.dq = dq; bp.dk = dk; bp.dv = dv;
     bp.bh_stride = g.N * g.d;
@@ -841,9 +845,10 @@ rehyat_status rehyat_attn_fwd_mlp_partials(const void* q, const void* k, const v
                           stream, phi_q, phi_k);
 }
 
-rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int dtype,
-                                  int B, int H, int frames, int tokens_per_frame, int head_dim, int chunk_frames,
-                                  int overlap_frames, int feature_map, int causal, void* stream) {
+rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  float* out_f32, int dtype, int B, int H, int frames, int tokens_per_frame,
+                                  int head_dim, int chunk_frames, int overlap_frames, int feature_map, int causal,
+                                  void* stream) {
     Geometry g{};
     rehyat_status st = check_common(g, B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
                                     feature_map, dtype);
@@ -856,16 +861,23 @@ rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, v
         overlaps(lse, lbytes, out, bytes) || overlaps(lse, lbytes, q, bytes) || overlaps(lse, lbytes, k, bytes) ||
         overlaps(lse, lbytes, v, bytes))
         return fail(REHYAT_EINVAL, "out and lse must not overlap q, k, v or each other");
+    if (out_f32 && dtype == REHYAT_BF16) {
+        const size_t fb = (size_t)g.BH * g.N * g.d * 4;
+        if (!aligned16(out_f32)) return fail(REHYAT_EINVAL, "out_f32 must be 16-byte aligned");
+        if (overlaps(out_f32, fb, q, bytes) || overlaps(out_f32, fb, k, bytes) || overlaps(out_f32, fb, v, bytes) ||
+            overlaps(out_f32, fb, out, bytes) || overlaps(out_f32, fb, lse, lbytes))
+            return fail(REHYAT_EINVAL, "out_f32 must not overlap the other tensors");
+    }
     g_last_error.clear();
     return run_fwd(q, k, v, out, g, causal ? kCausal : kBidirectional, nullptr, nullptr, nullptr, nullptr,
-                   nullptr, (hipStream_t)stream, nullptr, nullptr, lse);
+                   nullptr, (hipStream_t)stream, nullptr, nullptr, lse, out_f32);
 }
 
-rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                              const void* dout, void* dq, void* dk, void* dv, int dtype, int B, int H, int frames,
-                              int tokens_per_frame, int head_dim, int chunk_frames, int overlap_frames,
-                              int feature_map, int causal, void* stream) {
-    return bwd_entry(q, k, v, out, lse, dout, dq, dk, dv, dtype, B, H, frames, tokens_per_frame, head_dim,
+rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* out_f32,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv, int dtype, int B,
+                              int H, int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+                              int overlap_frames, int feature_map, int causal, void* stream) {
+    return bwd_entry(q, k, v, out, out_f32, lse, dout, dq, dk, dv, dtype, B, H, frames, tokens_per_frame, head_dim,
                      chunk_frames, overlap_frames, feature_map, causal ? kCausal : kBidirectional, stream);
 }
 

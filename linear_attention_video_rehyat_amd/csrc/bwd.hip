@@ -57,9 +57,11 @@ constexpr int kBwdKTile = 64;                  // keys per dq LDS tile
 // elu(x) + 1 and its derivative
 __device__ __forceinline__ float elu1_grad(float x) { return x > 0.0f ? 1.0f : __expf(x); }
 
-// dsum_i = dy_i . out_i: D/8 lanes per row (16 bytes each), reduced by shuffles.
-template <int D, typename T>
-__global__ __launch_bounds__(256) void dsum_kernel(const T* __restrict__ dy, const T* __restrict__ out,
+// dsum_i = dy_i . out_i: D/4 or D/8 lanes per row (16 bytes of dy each),
+// reduced by shuffles.  T: dy's type; U: out's (the bf16 path's fp32 copy of
+// the output, when the caller kept it, else bf16).
+template <int D, typename T, typename U>
+__global__ __launch_bounds__(256) void dsum_kernel(const T* __restrict__ dy, const U* __restrict__ out,
                                                    float* __restrict__ dsum, long long rows) {
     constexpr int EPL = 16 / sizeof(T);  // elements per lane
     constexpr int LPR = D / EPL;         // lanes per row
@@ -68,18 +70,22 @@ __global__ __launch_bounds__(256) void dsum_kernel(const T* __restrict__ dy, con
     const int part = (int)(g % LPR);
     float acc = 0.0f;
     if (row < rows) {
+        float x[EPL], y[EPL];
         const u32x4 a = *(const u32x4*)(dy + row * D + part * EPL);
-        const u32x4 b = *(const u32x4*)(out + row * D + part * EPL);
-        if constexpr (sizeof(T) == 2) {
-            float x[8], y[8];
-            unpack8(a, x);
-            unpack8(b, y);
+        if constexpr (sizeof(T) == 2) unpack8(a, x);
+        else
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
-        } else {
+            for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(a[e]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc += __uint_as_float(a[e]) * __uint_as_float(b[e]);
+        for (int o = 0; o < EPL * (int)sizeof(U) / 16; ++o) {
+            const u32x4 b = *(const u32x4*)(out + row * D + part * EPL + o * (16 / sizeof(U)));
+            if constexpr (sizeof(U) == 2) unpack8(b, y);
+            else
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[4 * o + e] = __uint_as_float(b[e]);
         }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc += x[e] * y[e];
     }
 #pragma unroll
     for (int o = LPR / 2; o >= 1; o /= 2) acc += __shfl_xor(acc, o, LPR);
@@ -788,24 +794,26 @@ hipError_t launch_f32_d(const BwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-template <typename T>
-static hipError_t dsum_typed(const BwdParams& p, float* dsum, hipStream_t s) {
+template <typename T, typename U>
+static hipError_t dsum_typed(const BwdParams& p, const U* out, float* dsum, hipStream_t s) {
     const long long rows = (long long)p.BH * p.N;
     const int epl = 16 / (int)sizeof(T);
     const long long threads = rows * (p.d / epl);
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     switch (p.d) {
-    case 16: dsum_kernel<16, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
-    case 32: dsum_kernel<32, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
-    case 64: dsum_kernel<64, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
-    case 128: dsum_kernel<128, T><<<blocks, 256, 0, s>>>((const T*)p.dy, (const T*)p.out, dsum, rows); break;
+    case 16: dsum_kernel<16, T, U><<<blocks, 256, 0, s>>>((const T*)p.dy, out, dsum, rows); break;
+    case 32: dsum_kernel<32, T, U><<<blocks, 256, 0, s>>>((const T*)p.dy, out, dsum, rows); break;
+    case 64: dsum_kernel<64, T, U><<<blocks, 256, 0, s>>>((const T*)p.dy, out, dsum, rows); break;
+    case 128: dsum_kernel<128, T, U><<<blocks, 256, 0, s>>>((const T*)p.dy, out, dsum, rows); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dsum(const BwdParams& p, float* dsum, bool bf16, hipStream_t s) {
-    return bf16 ? dsum_typed<uint16_t>(p, dsum, s) : dsum_typed<float>(p, dsum, s);
+    if (!bf16) return dsum_typed<float, float>(p, (const float*)p.out, dsum, s);
+    if (p.out_f32) return dsum_typed<uint16_t, float>(p, p.out_f32, dsum, s);
+    return dsum_typed<uint16_t, uint16_t>(p, (const uint16_t*)p.out, dsum, s);
 }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {

@@ -104,6 +104,8 @@ struct LocalParams {
     long long fq_bh_stride;
     // optional: ln(n^S + n^L) per query, fp32 [BH][n_rows] (the backward's normaliser)
     float* lse;
+    // optional (bf16 path): the output before rounding, fp32, same layout as out
+    float* out_f32;
 };
 
 // Key tiles of BN keys that a query tile of chunk t streams (its softmax window).
@@ -201,6 +203,7 @@ struct ScanParams {
 struct BwdParams {
     const void* q; const void* k; const void* v; const void* dy;  // [BH][N][d]
     const void* out;                                              // forward output (for dsum)
+    const float* out_f32;                                         // or its fp32 copy (bf16 path), preferred
     const float* lse; const float* dsum;                          // [BH][N]
     void* dq; void* dk; void* dv;
     long long bh_stride;                                          // N * d

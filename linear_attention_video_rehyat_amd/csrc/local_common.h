@@ -200,6 +200,8 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
                 }
                 u32x2 w = {pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
                 *(u32x2*)(ob_ptr + (long long)row * D + 32 * dt + 8 * g + 4 * h) = w;
+                if (p.out_f32)
+                    *(f32x4*)(p.out_f32 + prow * D + 32 * dt + 8 * g + 4 * h) = f32x4{y[0], y[1], y[2], y[3]};
             }
         } else {
 #pragma unroll

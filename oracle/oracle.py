@@ -363,3 +363,52 @@ def backward(q, k, v, dy, tokens_per_frame, chunk_frames, overlap_frames, phi="e
     y = (w @ V) / w.sum(dim=-1, keepdim=True)
     y.backward(G)
     return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+def grad_q_rows(q, k, v, dy, frames, tokens_per_frame, chunk_frames, overlap_frames, rows, phi="elu1",
+                causal=True):
+    """dq for selected query rows, straight from the definition (no autograd):
+    with the weights w_ij of §3.1-§3.3 (e^{q.k} on the softmax set, phi(q).phi(k)
+    on the linear set), N_i = sum_j w_ij, y_i = sum_j w_ij v_j / N_i and
+    g_ij = (dy_i . v_j - dy_i . y_i) / N_i,
+        dq_i = sum_{softmax j} w_ij g_ij k_j + phi'(q_i) * sum_{linear j} g_ij phi(k_j)
+    (phi' applied per feature: elu+1 -> 1 or e^x, the square -> 2x).  Each row
+    costs O(N (d + D')): usable at full workload size on a sample of rows.
+    Fixed feature maps only.  q, k, v, dy: [B, H, N, d]; returns [B, H, R, d]."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    B, H, N, d = q.shape
+    HW = tokens_per_frame
+    kind = phi_kind(phi)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((B, H, rows.size, d))
+    fk = feature_map(k, phi) if kind != PHI_NONE else None
+    for b in range(B):
+        for h in range(H):
+            for r, i in enumerate(rows):
+                t = (i // HW) // chunk_frames
+                w0 = max(t * chunk_frames - overlap_frames, 0) * HW
+                w1 = min((t + 1) * chunk_frames, frames) * HW
+                soft = np.arange(w0, w1)
+                lin = np.arange(0, w0) if causal else np.concatenate([np.arange(0, w0), np.arange(w1, N)])
+                qi, gi = q[b, h, i], dy[b, h, i]
+                ws = np.exp(k[b, h, soft] @ qi)
+                if kind != PHI_NONE and lin.size:
+                    fq = feature_map(qi[None], phi)[0]
+                    wl = fk[b, h, lin] @ fq
+                else:
+                    wl = np.zeros(0)
+                    lin = lin[:0]
+                n = ws.sum() + wl.sum()
+                y = (ws @ v[b, h, soft] + wl @ v[b, h, lin]) / n
+                dd = gi @ y
+                gs = (v[b, h, soft] @ gi - dd) / n
+                dq = (ws * gs) @ k[b, h, soft]
+                if lin.size:
+                    gl = (v[b, h, lin] @ gi - dd) / n
+                    dphi = gl @ fk[b, h, lin]
+                    e = np.where(qi > 0, 1.0, np.exp(np.minimum(qi, 0.0)))
+                    dq = dq + e * dphi[:d]
+                    if kind == PHI_POLY2:
+                        dq = dq + 2.0 * qi * dphi[d:]
+                out[b, h, r] = dq
+    return out

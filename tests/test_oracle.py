@@ -422,3 +422,18 @@ def test_gradient_of_v_sums_to_gradient_of_y():
     for phi in ("elu1", "poly2"):
         _, _, dv = O.backward(q, k, v, dy, 5, 2, 1, phi)
         np.testing.assert_allclose(dv.sum(axis=-2), dy.sum(axis=-2), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("phi", ["elu1", "poly2", "none"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_grad_q_rows_matches_reverse_mode(phi, causal):
+    """The per-row definition-form dq (usable at full size on sampled rows)
+    equals the reverse-mode gradient of the matrix form."""
+    rng = np.random.default_rng(24)
+    F, HW = 6, 5
+    q, k, v = rand_qkv(rng, 1, 2, F * HW, 4, kscale=0.6)
+    dy = rng.standard_normal(q.shape)
+    dq, _, _ = O.backward(q, k, v, dy, HW, 2, 1, phi, causal=causal)
+    rows = np.array([0, 3, 7, 12, 18, 29])
+    got = O.grad_q_rows(q, k, v, dy, F, HW, 2, 1, rows, phi, causal=causal)
+    np.testing.assert_allclose(got, dq[:, :, rows], rtol=1e-10, atol=1e-12)

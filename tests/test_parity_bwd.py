@@ -131,3 +131,30 @@ def test_bad_arguments():
         rh.attn_bwd(q, k, v, out, lse, out, 4, 16, 2, 1, "elu1", grads=(q, k, v))   # gradients alias inputs
     with pytest.raises(rh.RehyatError):
         rh.attn_bwd(q, k, v, out, lse[:, :, :-1].contiguous(), out, 4, 16, 2, 1, "elu1")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_wan_dq_sampled(causal):
+    """Full Wan2.1-1.3B shape, in the configuration bench.py times: dq of
+    seeded stratified rows (two per frame plus random ones, every chunk) against
+    the oracle's per-row definition-form gradient.  The row sums D = dy . y come
+    from the fp32 output (the bf16 output alone puts the bidirectional dq at
+    the edge of the bar, see include/rehyat.h)."""
+    from tests.parity_util import sample_rows
+    w = inputs.WORKLOADS["wan_21x30x52"]
+    q, k, v = inputs.make_qkv(w)
+    dy = inputs.make_dout(w)
+    qg, kg, vg, dyg = gpu(q, k, v, dy)
+    out, lse, out32 = rh.attn_fwd_lse(qg, kg, vg, w.frames, w.tokens_per_frame, 3, 1, "elu1", causal=causal,
+                                      out_f32=True)
+    assert torch.equal(out32.to(torch.bfloat16), out)
+    dq, _, _ = rh.attn_bwd(qg, kg, vg, out, lse, dyg, w.frames, w.tokens_per_frame, 3, 1, "elu1", causal=causal,
+                           out_f32=out32)
+    sync()
+    rows = sample_rows(w.frames, w.tokens_per_frame, n_random=24, seed=31)
+    ref = O.grad_q_rows(to64(q), to64(k), to64(v), to64(dy), w.frames, w.tokens_per_frame, 3, 1, rows, "elu1",
+                        causal=causal)
+    got = to64(dq[:, :, torch.from_numpy(rows).to("cuda")])
+    e = rel_l2(got, ref)
+    a = float(np.abs(got - ref).max() / np.abs(ref).max())
+    assert e <= 1e-2 and a <= 3e-2, f"rel-L2 {e:.3e}, max-abs/scale {a:.3e}"
