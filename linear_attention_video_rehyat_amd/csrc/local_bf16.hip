@@ -303,6 +303,9 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         shi = (const uint16_t*)p.s_hi + bh * p.s_bh_stride + t * p.s_chunk_stride;
         slo = (const uint16_t*)p.s_lo + bh * p.s_bh_stride + t * p.s_chunk_stride;
     }
+    // waves whose query rows all lie past the chunk end (in the chunk's last,
+    // partial tile) only take their share of the loads and the barriers
+    const bool active = q_start + wave * QB * 32 < q_end;
     auto iteration = [&](int it, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
         if (it + PF < ntiles)
             issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(fill, wave, it + PF, p.prev_rows, seg_shift, rb, op_row,
@@ -311,8 +314,10 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
             issue_state_dma<D, DP, NW>(fill, wave, lane, shi);
             if (S_ONE_SLOT) issue_state_dma<D, DP, NW>(fill + SPART, wave, lane, slo);
         }
-        scores_softmax(it, cur);
-        pv(cur + KTILE);
+        if (active) {
+            scores_softmax(it, cur);
+            pv(cur + KTILE);
+        }
     };
     for (int it = 0; it < ntiles; ++it) {
         // own loads of tile `it` have landed (tiles it+1 .. it+PF-1 may still be
@@ -344,6 +349,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         lds_barrier();                               // everyone's
         s_lds = hi_slot;
     }
+    if (!active) return;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
         finish_query_block<D, PHI>(p, qreg[qb], oacc[qb], msum[qb], m2[qb], mtrue[qb],
