@@ -66,10 +66,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
             *(f32x4*)(p.z + off) = x;
         }
     };
+    // the sub-blocks' loads of a block sum are issued together (up to 4)
     auto block_sum = [&](int u) {
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < p.n_sub; ++sp) d += *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
-        return d;
+        f32x4 d[4];
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp)
+            d[sp] = sp < p.n_sub ? *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 b = d[0] + d[1] + d[2] + d[3];
+        for (int sp = 4; sp < p.n_sub; ++sp) b += *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
+        return b;
     };
     if (p.mode == kChunkRows) {
         // suffix sums: slot u gets the blocks u .. U-1
@@ -127,8 +133,31 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
         }
         return;
     }
-    // blocks of 4 delta blocks: their loads are issued together (the chain of
-    // adds is short; the latency of the loads is what costs)
+    // The latency of the loads is what costs, not the short chain of adds:
+    // up to 8 delta blocks of up to 4 sub-blocks, every load is issued at once
+    constexpr int MAXU = 8, MAXS = 4;
+    if (p.U <= MAXU && p.n_sub <= MAXS) {
+        f32x4 d[MAXU][MAXS];
+#pragma unroll
+        for (int u = 0; u < MAXU; ++u)
+#pragma unroll
+            for (int sp = 0; sp < MAXS; ++sp)
+                d[u][sp] = u < p.U && sp < p.n_sub ? *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride)
+                                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < MAXU; ++u) {
+            if (u >= p.U) break;
+            emit(u);
+            f32x4 b = d[u][0];
+#pragma unroll
+            for (int sp = 1; sp < MAXS; ++sp) b += d[u][sp];
+            x += b;
+        }
+        emit(p.U);
+        if (p.state_out) *(f32x4*)(p.state_out + (long long)bh * E + e4) = x;
+        return;
+    }
+    // otherwise blocks of 4 delta blocks, their loads issued together
     for (int u0 = 0; u0 < p.U; u0 += 4) {
         f32x4 d[4];
 #pragma unroll
