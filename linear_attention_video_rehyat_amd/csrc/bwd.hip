@@ -18,38 +18,38 @@
 // its second operand, and a suffix scan.
 //
 // bf16 kernels, both on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
-//  * dk/dv: a workgroup of 4 waves owns 128 keys (32 per wave, their K and V
-//    fragments in registers) and streams the query rows of the chunks whose
-//    windows hold them (64-row Q and dY tiles in a 2-stage LDS ring, with each
-//    row's lse, D and window bounds).  Per 32 queries: S = Q K^T and dP = dY V^T
-//    (keys in the lane dimension), P and dS in registers, then dV^T += dY^T P
-//    and dK^T += Q^T dS with dY^T and Q^T read through the transposing LDS read
-//    in the key order of P's registers.  The linear branch of the wave's keys
-//    is added at the end from G_u (both layouts, bf16 hi/lo) and g_u.
-//  * dq: a workgroup of 4 waves owns 128 queries of one chunk (q and dy
+//  * dk/dv: a workgroup of 8 waves owns 128 keys and streams the query rows of
+//    the chunks whose windows hold them (64-row Q and dY tiles in a 3-stage LDS
+//    ring, with each row's lse, D and window bounds).  Two waves share 32 keys
+//    (one per lane): the first holds their K fragments and forms S = Q K^T, P
+//    and dV^T += dY^T P, and passes P (bf16) through LDS to the second, which
+//    holds V, runs one tile behind and forms dP = dY V^T, dS = P (dP - D) and
+//    dK^T += Q^T dS.  dY^T and Q^T come through the transposing LDS read in the
+//    key order of P's registers.  The linear branch of the keys is added first
+//    from G_u (both layouts, bf16 hi/lo) and g_u.
+//  * dq: a workgroup of 8 waves owns 256 queries of one chunk (q and dy
 //    fragments in registers) and streams its window's K and V tiles (64 keys,
-//    2-stage ring).  Per 32 keys: S^T = K Q^T, dP^T = V dY^T, dS^T in registers,
-//    dQ^T += K^T dS^T (K^T by the transposing read).  The linear branch is added
-//    at the end from S_t (transposed layout, bf16 hi/lo) and z_t.
+//    2-stage ring).  Per 64-key tile: S^T = K Q^T and dP^T = V dY^T of both
+//    32-key halves (four independent MFMA chains), dS^T in registers,
+//    dQ^T += K^T dS^T (K^T by the transposing read).  The linear branch is
+//    added at the end from S_t (transposed layout, bf16 hi/lo) and z_t.
 // fp32 kernels: the same sums on the vector ALU (one query or key per lane).
+#include <type_traits>
+
 #include "local_common.h"
 
 namespace rehyat {
 
 namespace {
 
-#ifndef REHYAT_BWD_KWAVES
-#define REHYAT_BWD_KWAVES 4
-#endif
 #ifndef REHYAT_BWD_QWAVES
 #define REHYAT_BWD_QWAVES 8
 #endif
 #ifndef REHYAT_BWD_QROWS
 #define REHYAT_BWD_QROWS 64
 #endif
-constexpr int kBwdKWaves = REHYAT_BWD_KWAVES;  // waves of a dk/dv workgroup (32 keys each)
 constexpr int kBwdQWaves = REHYAT_BWD_QWAVES;  // waves of a dq workgroup (32 queries each)
-constexpr int kBwdKeys = 32 * kBwdKWaves;      // keys per dk/dv workgroup
+constexpr int kBwdKeys = 128;                  // keys per dk/dv workgroup (4 pairs of waves)
 constexpr int kBwdQRows = REHYAT_BWD_QROWS;    // query rows per dk/dv LDS tile
 constexpr int kBwdQueries = 32 * kBwdQWaves;   // queries per dq workgroup
 constexpr int kBwdKTile = 64;                  // keys per dq LDS tile
@@ -115,9 +115,20 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
 }
 
 // ------------------------------------------------------------------ dk / dv (bf16)
+// Each workgroup owns 128 keys and streams the query rows of the chunks whose
+// windows hold them.  The work of a key is split over two waves: 4 pairs of
+// waves, pair w owning keys kb0 + 32 w .. + 31 (one per lane).  The
+// first wave of a pair forms S^T = K Q^T, P = exp(S - lse) on the key's
+// windows and dV^T += dY^T P, and hands P (bf16, in the MFMA output layout) to
+// the second wave through LDS; the second, one query tile behind, forms
+// dP^T = V dY^T, dS = P (dP - dsum) and dK^T += Q^T dS.  Each wave holds one of
+// K and V and one of the dV and dK accumulators, so two waves fit per SIMD and
+// the vector work of one overlaps the products of the other.  Query tiles
+// stream through a 3-stage LDS ring (the second wave reads the tile before).
 template <int D, int PHI>
-__global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p) {
-    constexpr int NW = kBwdKWaves, BQ = kBwdQRows;
+__global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
+    constexpr int NP = 4, NW = 2 * NP, BQ = kBwdQRows, NST = 3, NQS = BQ / 32;
+    static_assert(32 * NP == kBwdKeys, "a pair of waves per 32 keys of the block");
     constexpr int C = D / 8, KS = D / 16, DT = D / 32;
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     constexpr int KSL = DP / 16, FT = DP / 32;
@@ -125,18 +136,21 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
     constexpr int NI = QT * 2 / 1024;                  // 1 KB loads per tile
     constexpr int OPW = 2 * NI / NW;                   // per wave, Q and dY
     static_assert(2 * NI % NW == 0, "tile loads must split evenly");
-    __shared__ __attribute__((aligned(16))) uint16_t tiles_raw[2][2 * QT];
-    __shared__ __attribute__((aligned(16))) float rowf[2][2][BQ];   // lse log2(e), dsum
-    __shared__ __attribute__((aligned(16))) int roww[2][2][BQ];     // window bounds
+    __shared__ __attribute__((aligned(16))) uint16_t tiles_raw[NST][2 * QT];
+    __shared__ __attribute__((aligned(16))) u32x4 pbuf[2][NP][NQS][2][64];  // P of a tile, per pair
+    __shared__ __attribute__((aligned(16))) float rowf[NST][2][BQ];        // lse log2(e), dsum
+    __shared__ __attribute__((aligned(16))) int roww[NST][2][BQ];          // window bounds
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool first = wave < NP;                      // S, P, dV (else dP, dS, dK)
+    const int pair = wave % NP;
     const int h = lane >> 5, lq = lane & 31;
     const int nkb = (p.N + kBwdKeys - 1) / kBwdKeys;
     const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
     const int bh = item / nkb;
     const int kb0 = (item - bh * nkb) * kBwdKeys;
-    const int key = kb0 + 32 * wave + lq;              // the lane's key (column of every tile)
+    const int key = kb0 + 32 * pair + lq;              // the lane's key (column of every tile)
     const bool key_ok = key < p.N;
     const int keyc = min(key, p.N - 1);
 
@@ -147,11 +161,12 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
     const float* lseb = p.lse + (long long)bh * p.N;
     const float* dsb = p.dsum + (long long)bh * p.N;
 
-    bf16x8 kf[KS], vf[KS];
+    // the first wave of a pair holds K of its keys, the second V
+    bf16x8 kv[KS];
+    {
+        const uint16_t* src = (first ? kbp : vbp) + (long long)keyc * D + 8 * h;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        kf[s] = __builtin_bit_cast(bf16x8, ldg_b128(kbp + (long long)keyc * D + 16 * s + 8 * h));
-        vf[s] = __builtin_bit_cast(bf16x8, ldg_b128(vbp + (long long)keyc * D + 16 * s + 8 * h));
+        for (int s = 0; s < KS; ++s) kv[s] = __builtin_bit_cast(bf16x8, ldg_b128(src + 16 * s));
     }
 
     // query rows of the chunks whose windows hold any of the block's keys
@@ -165,7 +180,7 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
     const int rb = D * 2;
     const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, qr1 * rb, 0x00020000);
     const __amdgpu_buffer_rsrc_t dyrs = __builtin_amdgcn_make_buffer_rsrc((void*)dyb, (short)0, qr1 * rb, 0x00020000);
-    auto load_tile = [&](int buf, int it) {
+    auto load_tile = [&](int st, int it) {
         const int r0 = qr0 + it * BQ;
 #pragma unroll
         for (int o = 0; o < OPW; ++o) {
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
             const int off = (r0 + r) * rb + ((pos % C) ^ swz<C>(r)) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(isdy ? dyrs : qrs,
                                                      (__attribute__((address_space(3))) void*)(
-                                                         (lds_u16*)tiles_raw[buf] + (isdy ? QT : 0) + 512 * ins),
+                                                         (lds_u16*)tiles_raw[st] + (isdy ? QT : 0) + 512 * ins),
                                                      16, off, 0, 0, 0);
         }
     };
@@ -198,11 +213,11 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
             rw0 = rw1 = 0;  // no key lies in an empty window
         }
     };
-    auto store_rows = [&](int buf) {
-        rowf[buf][0][64 * wave + lane] = rl;
-        rowf[buf][1][64 * wave + lane] = rd;
-        roww[buf][0][64 * wave + lane] = rw0;
-        roww[buf][1][64 * wave + lane] = rw1;
+    auto store_rows = [&](int st) {
+        rowf[st][0][64 * wave + lane] = rl;
+        rowf[st][1][64 * wave + lane] = rd;
+        roww[st][0][64 * wave + lane] = rw0;
+        roww[st][1][64 * wave + lane] = rw1;
     };
 
     // transposing-read offsets (dY^T / Q^T fragments: lane row d = 32 c + lq,
@@ -218,19 +233,15 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
         toff[c][1] = (tr_row + 8) * D + ((ch ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
     }
 
-    f32x16 dvt[DT], dkt[DT];
+    f32x16 acc[DT];  // dV^T (first wave) or dK^T (second)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        dvt[dt] = f32x16{};
-        dkt[dt] = f32x16{};
-    }
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-    // ---- linear branch of the wave's keys (delta blocks u <= C-2), first: its
-    // temporaries are dead before the main loop needs its registers
+    // ---- linear branch of the keys (delta blocks u <= C-2, or the 2C+1
+    // bidirectional blocks): dv += G_u^T phi(k) on the first wave, dk from
+    // dphi(k) = G_u v - g_u on the second
     if constexpr (PHI != kPhiNone) {
         if (p.lin) {
-            // block of the key: delta block E_u (recurrent form; u <= C-2 has a
-            // gradient sum) or bidirectional block b (2C+1 of them)
             const bool bidir = p.mode == kBidirectional;
             const int u_key = bidir ? bidir_block_of_frame(keyc / p.HW, p.Tc, p.To) : (keyc / p.HW + p.To) / p.Tc;
             const int u_first = __builtin_amdgcn_readfirstlane(u_key);
@@ -240,72 +251,216 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
             for (int u = u_first; u <= u_last && u <= u_max; ++u) {
                 const bool mine = key_ok && u_key == u;
                 const long long sofs = (long long)bh * slots * p.s_stride + (long long)u * p.s_stride;
-                const uint16_t* ghi = (const uint16_t*)p.g_hi + sofs;
-                const uint16_t* glo = (const uint16_t*)p.g_lo + sofs;
-                const uint16_t* gthi = (const uint16_t*)p.gt_hi + sofs;
-                const uint16_t* gtlo = (const uint16_t*)p.gt_lo + sofs;
-                const float* gz = p.gz + (long long)bh * slots * p.z_stride + (long long)u * p.z_stride;
-                // dv += G_u^T phi(k): A = G_u^T rows (d), B = phi(k) (masked to the block's keys);
-                // one output tile at a time (unrolled, the loads of every tile would be
-                // hoisted and held in registers)
+                if (first) {
+                    const uint16_t* ghi = (const uint16_t*)p.g_hi + sofs;
+                    const uint16_t* glo = (const uint16_t*)p.g_lo + sofs;
 #pragma unroll 1
-                for (int dt = 0; dt < DT; ++dt) {
-                    f32x16 acc = f32x16{};
+                    for (int dt = 0; dt < DT; ++dt) {
+                        f32x16 a = f32x16{};
 #pragma unroll
-                    for (int ksl = 0; ksl < KSL; ++ksl) {
-                        float x[8], f[8];
-                        unpack8(__builtin_bit_cast(u32x4, kf[ksl % KS]), x);
+                        for (int ksl = 0; ksl < KSL; ++ksl) {
+                            // phi(k) is recomputed for every output tile: held
+                            // for all of them it would not fit in the registers
+                            u32x4 kx = __builtin_bit_cast(u32x4, kv[ksl % KS]);
+                            asm volatile("" : "+v"(kx));
+                            float x[8], f[8];
+                            unpack8(kx, x);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) f[e] = mine ? (ksl < KS ? elu1(x[e]) : x[e] * x[e]) : 0.0f;
-                        u32x4 whi, wlo;
+                            for (int e = 0; e < 8; ++e) f[e] = mine ? (ksl < KS ? elu1(x[e]) : x[e] * x[e]) : 0.0f;
+                            u32x4 whi, wlo;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float h0 = round_bf16(f[2 * e]), h1 = round_bf16(f[2 * e + 1]);
-                            whi[e] = pack2_bf16(h0, h1);
-                            wlo[e] = pack2_bf16(f[2 * e] - h0, f[2 * e + 1] - h1);
+                            for (int e = 0; e < 4; ++e) {
+                                const float h0 = round_bf16(f[2 * e]), h1 = round_bf16(f[2 * e + 1]);
+                                whi[e] = pack2_bf16(h0, h1);
+                                wlo[e] = pack2_bf16(f[2 * e] - h0, f[2 * e + 1] - h1);
+                            }
+                            const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
+                            const bf16x8 ah = __builtin_bit_cast(bf16x8, ldg_b128(ghi + off));
+                            const bf16x8 al = __builtin_bit_cast(bf16x8, ldg_b128(glo + off));
+                            const bf16x8 fh = __builtin_bit_cast(bf16x8, whi), fl = __builtin_bit_cast(bf16x8, wlo);
+                            a = mfma32x32x16(ah, fh, a);
+                            a = mfma32x32x16(al, fh, a);
+                            a = mfma32x32x16(ah, fl, a);
                         }
-                        const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
-                        const bf16x8 ah = __builtin_bit_cast(bf16x8, ldg_b128(ghi + off));
-                        const bf16x8 al = __builtin_bit_cast(bf16x8, ldg_b128(glo + off));
-                        const bf16x8 fh = __builtin_bit_cast(bf16x8, whi), fl = __builtin_bit_cast(bf16x8, wlo);
-                        acc = mfma32x32x16(ah, fh, acc);
-                        acc = mfma32x32x16(al, fh, acc);
-                        acc = mfma32x32x16(ah, fl, acc);
-                    }
 #pragma unroll
-                    for (int x = 0; x < DT; ++x)  // static register indices (dt is not unrolled)
-                        if (x == dt) dvt[x] += acc;
-                }
-                // dphi(k) = G_u v - g_u: A = G_u rows (features), B = V^T (the lane's key)
+                        for (int x = 0; x < DT; ++x)  // static register indices (dt is not unrolled)
+                            if (x == dt) acc[x] += a;
+                    }
+                } else {
+                    const uint16_t* gthi = (const uint16_t*)p.gt_hi + sofs;
+                    const uint16_t* gtlo = (const uint16_t*)p.gt_lo + sofs;
+                    const float* gz = p.gz + (long long)bh * slots * p.z_stride + (long long)u * p.z_stride;
 #pragma unroll 1
-                for (int ft = 0; ft < FT; ++ft) {
-                    f32x16 acc = f32x16{};
+                    for (int ft = 0; ft < FT; ++ft) {
+                        f32x16 a = f32x16{};
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) {
-                        const long long off = (long long)(32 * ft + lq) * D + 16 * s + 8 * h;
-                        acc = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(gthi + off)), vf[s], acc);
-                        acc = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(gtlo + off)), vf[s], acc);
+                        for (int s = 0; s < KS; ++s) {
+                            const long long off = (long long)(32 * ft + lq) * D + 16 * s + 8 * h;
+                            a = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(gthi + off)), kv[s], a);
+                            a = mfma32x32x16(__builtin_bit_cast(bf16x8, ldg_b128(gtlo + off)), kv[s], a);
+                        }
+                        if (!mine) continue;
+                        const int dt = ft % DT;
+                        f32x16 add;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int f0 = 32 * ft + 8 * j + 4 * h;          // features f0 .. f0+3
+                            const int d0 = 32 * dt + 8 * j + 4 * h;          // their head_dim rows
+                            const f32x4 g4 = *(const f32x4*)(gz + f0);
+                            float kx[4];
+                            load4_bf16(kbp + (long long)keyc * D + d0, kx);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) add[4 * j + i] = feature_grad<D>(f0 + i, kx[i], a[4 * j + i] - g4[i]);
+                        }
+#pragma unroll
+                        for (int x = 0; x < DT; ++x)
+                            if (x == dt) acc[x] += add;
                     }
-                    if (!mine) continue;
-                    const int dt = ft % DT;
-                    f32x16 add;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int f0 = 32 * ft + 8 * j + 4 * h;          // features f0 .. f0+3
-                        const int d0 = 32 * dt + 8 * j + 4 * h;          // their head_dim rows
-                        const f32x4 g4 = *(const f32x4*)(gz + f0);
-                        float kx[4];
-                        load4_bf16(kbp + (long long)keyc * D + d0, kx);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) add[4 * j + i] = feature_grad<D>(f0 + i, kx[i], acc[4 * j + i] - g4[i]);
-                    }
-#pragma unroll
-                    for (int x = 0; x < DT; ++x)
-                        if (x == dt) dkt[x] += add;
                 }
             }
         }
     }
+
+    // first wave, tile t: S^T, P (masked to the windows), P to LDS, dV^T += dY^T P
+    // (FULL: every key of the block lies in the window of every row of the tile,
+    // no masking needed; one instance each, so that neither has a branch inside)
+    auto first_step = [&](int t, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        // lane addressing re-derived per step behind an empty asm, so that the
+        // compiler does not keep every read's address live across the loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int h = ln >> 5, lq = ln & 31;
+        int toff[DT][2];
+        {
+            const int tr_row = 4 * h + ((ln & 15) >> 2);
+            const int tr_chunk = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+            const int tr_sub = 4 * (ln & 1);
+#pragma unroll
+            for (int c = 0; c < DT; ++c) {
+                const int ch = 4 * c + tr_chunk;
+                toff[c][0] = tr_row * D + ((ch ^ swz<C>(tr_row)) << 3) + tr_sub;
+                toff[c][1] = (tr_row + 8) * D + ((ch ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
+            }
+        }
+        const int st = t % NST;
+        const lds_u16* Qs = (const lds_u16*)tiles_raw[st];
+        const lds_u16* Ys = Qs + QT;
+        // the subtiles' S^T chains side by side (independent accumulators)
+        f32x16 sall[NQS];
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) sall[qs] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int qs = 0; qs < NQS; ++qs) {
+                const int arow = 32 * qs + lq;
+                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
+                sall[qs] = mfma32x32x16(lds_read_b128(Qs, off), kv[s], sall[qs]);
+            }
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) {
+            const f32x16& sacc = sall[qs];
+            // rows 32 qs + 8 j + 4 h + i of the tile, column = the lane's key
+            u32x4 pw[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = 32 * qs + 8 * j + 4 * h;
+                const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[st][0][r0];
+                float pv[4];
+                if constexpr (FULL) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - l4[i]);
+                } else {
+                    typedef int i32x4 __attribute__((ext_vector_type(4)));
+                    const i32x4 a4 = *(const __attribute__((address_space(3))) i32x4*)&roww[st][0][r0];
+                    const i32x4 b4 = *(const __attribute__((address_space(3))) i32x4*)&roww[st][1][r0];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool in = key_ok && key >= a4[i] && key < b4[i];
+                        pv[i] = in ? __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - l4[i]) : 0.0f;
+                    }
+                }
+                pw[j >> 1][2 * (j & 1)] = pack2_bf16(pv[0], pv[1]);
+                pw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(pv[2], pv[3]);
+            }
+            pbuf[t & 1][pair][qs][0][ln] = pw[0];
+            pbuf[t & 1][pair][qs][1][ln] = pw[1];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r16 = (32 * qs + 16 * kk) * D;
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x8 ya = cat(lds_read_tr(Ys, r16 + toff[dt][0]), lds_read_tr(Ys, r16 + toff[dt][1]));
+                    acc[dt] = mfma32x32x16(ya, pb, acc[dt]);
+                }
+            }
+        }
+    };
+    // second wave, tile t: dP^T, dS = P (dP - dsum) with the first wave's P, dK^T += Q^T dS
+    auto second_step = [&](int t) {
+        // lane addressing re-derived per step behind an empty asm, so that the
+        // compiler does not keep every read's address live across the loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int h = ln >> 5, lq = ln & 31;
+        int toff[DT][2];
+        {
+            const int tr_row = 4 * h + ((ln & 15) >> 2);
+            const int tr_chunk = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+            const int tr_sub = 4 * (ln & 1);
+#pragma unroll
+            for (int c = 0; c < DT; ++c) {
+                const int ch = 4 * c + tr_chunk;
+                toff[c][0] = tr_row * D + ((ch ^ swz<C>(tr_row)) << 3) + tr_sub;
+                toff[c][1] = (tr_row + 8) * D + ((ch ^ swz<C>(tr_row + 8)) << 3) + tr_sub;
+            }
+        }
+        const int st = t % NST;
+        const lds_u16* Qs = (const lds_u16*)tiles_raw[st];
+        const lds_u16* Ys = Qs + QT;
+        f32x16 pall[NQS];
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) pall[qs] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int qs = 0; qs < NQS; ++qs) {
+                const int arow = 32 * qs + lq;
+                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
+                pall[qs] = mfma32x32x16(lds_read_b128(Ys, off), kv[s], pall[qs]);
+            }
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) {
+            const f32x16& pacc = pall[qs];
+            const u32x4 pw[2] = {pbuf[t & 1][pair][qs][0][ln], pbuf[t & 1][pair][qs][1][ln]};
+            u32x4 dw[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = 32 * qs + 8 * j + 4 * h;
+                const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[st][1][r0];
+                const uint32_t w0 = pw[j >> 1][2 * (j & 1)], w1 = pw[j >> 1][2 * (j & 1) + 1];
+                const float pv[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
+                                     __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
+                float dv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dv[i] = pv[i] * (pacc[4 * j + i] - d4[i]);
+                dw[j >> 1][2 * (j & 1)] = pack2_bf16(dv[0], dv[1]);
+                dw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(dv[2], dv[3]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r16 = (32 * qs + 16 * kk) * D;
+                const bf16x8 db = __builtin_bit_cast(bf16x8, dw[kk]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x8 qa = cat(lds_read_tr(Qs, r16 + toff[dt][0]), lds_read_tr(Qs, r16 + toff[dt][1]));
+                    acc[dt] = mfma32x32x16(qa, db, acc[dt]);
+                }
+            }
+        }
+    };
 
     if (ntiles > 0) {
         load_tile(0, 0);
@@ -314,95 +469,47 @@ __global__ __launch_bounds__(kBwdKWaves * 64) void dkdv_bf16_kernel(BwdParams p)
             store_rows(0);
         }
     }
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    // iteration it: the first waves take tile it, the second waves tile it - 1;
+    // the ring holds tiles it - 1, it and (being loaded) it + 1
+    for (int it = 0; it <= ntiles && ntiles > 0; ++it) {
+        // own loads of tile it and own LDS writes (P, row data) have landed,
+        // then every wave's have
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
         lds_barrier();
         const bool more = it + 1 < ntiles;
         if (more) {
-            load_tile(buf ^ 1, it + 1);
+            load_tile((it + 1) % NST, it + 1);
             if (wave < RW) fetch_rows(it + 1);
         }
-        const lds_u16* Qs = (const lds_u16*)tiles_raw[buf];
-        const lds_u16* Ys = Qs + QT;
-        // every key of the block lies in the window of every row of the tile
-        // (windows move forward with the row): no masking needed
-        bool full;
-        {
-            const int ia = qr0 + it * BQ, ib = ia + BQ - 1;
-            int a0, a1, b0, b1;
-            row_window(p, ia, a0, a1);
-            row_window(p, ib, b0, b1);
-            full = ib < qr1 && kb0 + kBwdKeys <= p.N && b0 <= kb0 && a1 >= kb0 + kBwdKeys;
+        if (first) {
+            if (it < ntiles) {
+                // windows move forward with the row: the tile needs no mask when
+                // its first row's window ends after the block and its last row's
+                // starts before it
+                const int ia = qr0 + it * BQ, ib = ia + BQ - 1;
+                int a0, a1, b0, b1;
+                row_window(p, ia, a0, a1);
+                row_window(p, ib, b0, b1);
+                if (ib < qr1 && kb0 + kBwdKeys <= p.N && b0 <= kb0 && a1 >= kb0 + kBwdKeys)
+                    first_step(it, std::true_type{});
+                else
+                    first_step(it, std::false_type{});
+            }
+        } else {
+            if (it > 0) second_step(it - 1);
         }
-#pragma unroll
-        for (int qs = 0; qs < BQ / 32; ++qs) {
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-            const int arow = 32 * qs + lq;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
-                sacc = mfma32x32x16(lds_read_b128(Qs, off), kf[s], sacc);
-                pacc = mfma32x32x16(lds_read_b128(Ys, off), vf[s], pacc);
-            }
-            // rows 32 qs + 8 j + 4 h + i of the tile, column = the lane's key
-            u32x4 pw[2], dw[2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r0 = 32 * qs + 8 * j + 4 * h;
-                const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][0][r0];
-                const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)&rowf[buf][1][r0];
-                float pv[4], dv[4];
-                if (full) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - l4[i]);
-                } else {
-                    typedef int i32x4 __attribute__((ext_vector_type(4)));
-                    const i32x4 a4 = *(const __attribute__((address_space(3))) i32x4*)&roww[buf][0][r0];
-                    const i32x4 b4 = *(const __attribute__((address_space(3))) i32x4*)&roww[buf][1][r0];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool in = key_ok && key >= a4[i] && key < b4[i];
-                        pv[i] = in ? __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - l4[i]) : 0.0f;
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dv[i] = pv[i] * (pacc[4 * j + i] - d4[i]);
-                pw[j >> 1][2 * (j & 1)] = pack2_bf16(pv[0], pv[1]);
-                pw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(pv[2], pv[3]);
-                dw[j >> 1][2 * (j & 1)] = pack2_bf16(dv[0], dv[1]);
-                dw[j >> 1][2 * (j & 1) + 1] = pack2_bf16(dv[2], dv[3]);
-            }
-            // dV^T += dY^T P, dK^T += Q^T dS over the subtile's 32 queries (two 16-row steps)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int r16 = (32 * qs + 16 * kk) * D;
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
-                const bf16x8 db = __builtin_bit_cast(bf16x8, dw[kk]);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const bf16x8 ya = cat(lds_read_tr(Ys, r16 + toff[dt][0]), lds_read_tr(Ys, r16 + toff[dt][1]));
-                    const bf16x8 qa = cat(lds_read_tr(Qs, r16 + toff[dt][0]), lds_read_tr(Qs, r16 + toff[dt][1]));
-                    dvt[dt] = mfma32x32x16(ya, pb, dvt[dt]);
-                    dkt[dt] = mfma32x32x16(qa, db, dkt[dt]);
-                }
-            }
-        }
-        if (more && wave < RW) store_rows(buf ^ 1);
+        if (more && wave < RW) store_rows((it + 1) % NST);
     }
 
     if (!key_ok) return;
-    uint16_t* dkp = (uint16_t*)p.dk + bh * p.bh_stride + (long long)key * D;
-    uint16_t* dvp = (uint16_t*)p.dv + bh * p.bh_stride + (long long)key * D;
+    uint16_t* dst = (uint16_t*)(first ? p.dv : p.dk) + bh * p.bh_stride + (long long)key * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int d0 = 32 * dt + 8 * j + 4 * h;
-            *(u32x2*)(dkp + d0) = u32x2{pack2_bf16(dkt[dt][4 * j], dkt[dt][4 * j + 1]),
-                                        pack2_bf16(dkt[dt][4 * j + 2], dkt[dt][4 * j + 3])};
-            *(u32x2*)(dvp + d0) = u32x2{pack2_bf16(dvt[dt][4 * j], dvt[dt][4 * j + 1]),
-                                        pack2_bf16(dvt[dt][4 * j + 2], dvt[dt][4 * j + 3])};
+            *(u32x2*)(dst + d0) = u32x2{pack2_bf16(acc[dt][4 * j], acc[dt][4 * j + 1]),
+                                        pack2_bf16(acc[dt][4 * j + 2], acc[dt][4 * j + 3])};
         }
 }
 
@@ -494,16 +601,24 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
         if (it + 1 < ntiles) load_tile(buf ^ 1, it + 1);
         const lds_u16* Ks = (const lds_u16*)tiles_raw[buf];
         const lds_u16* Vs = Ks + KT;
+        // the S^T and dP^T chains of every 32-key subtile side by side
+        constexpr int NKS = BN / 32;
+        f32x16 sall[NKS], pall[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) sall[ks] = pall[ks] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int arow = 32 * ks + lq;
+                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
+                sall[ks] = mfma32x32x16(lds_read_b128(Ks, off), qf[s], sall[ks]);
+                pall[ks] = mfma32x32x16(lds_read_b128(Vs, off), yf[s], pall[ks]);
+            }
 #pragma unroll
         for (int ks = 0; ks < BN / 32; ++ks) {
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-            const int arow = 32 * ks + lq;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int off = arow * D + (((2 * s + h) ^ swz<C>(arow)) << 3);
-                sacc = mfma32x32x16(lds_read_b128(Ks, off), qf[s], sacc);
-                pacc = mfma32x32x16(lds_read_b128(Vs, off), yf[s], pacc);
-            }
+            const f32x16& sacc = sall[ks];
+            const f32x16& pacc = pall[ks];
             // key rows 32 ks + 8 j + 4 h + i of the tile, column = the lane's query
             u32x4 dw[2];
 #pragma unroll
@@ -757,7 +872,7 @@ hipError_t launch_bf16_dp(const BwdParams& p, hipStream_t s) {
     const long long kblocks = (long long)p.BH * ((p.N + kBwdKeys - 1) / kBwdKeys);
     const int tpc = dq_tiles_per_chunk(p, kBwdQueries);
     const long long qblocks = (long long)p.BH * p.C * tpc;
-    if (kblocks > 0) dkdv_bf16_kernel<D, PHI><<<(unsigned)kblocks, kBwdKWaves * 64, 0, s>>>(p);
+    if (kblocks > 0) dkdv_bf16_kernel<D, PHI><<<(unsigned)kblocks, 512, 0, s>>>(p);
     if (qblocks > 0) dq_bf16_kernel<D, PHI><<<(unsigned)qblocks, kBwdQWaves * 64, 0, s>>>(p, tpc);
     return hipGetLastError();
 }
