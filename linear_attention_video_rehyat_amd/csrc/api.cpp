@@ -65,6 +65,14 @@ SubSplit state_split(int dtype, long long rows) {
     return {(int)n, sub};
 }
 
+// Workgroups per (b, h) of a block-state launch: the sub-blocks of every block.
+int state_items_per_bh(const StateParams& sp) {
+    const BlockPart part = state_part(sp);
+    int n = 0;
+    for (int u = 0; u < sp.n_blocks; ++u) n += part_block_subs(part, u);
+    return n;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool bf16_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
@@ -329,12 +337,13 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
             sp.fk = ws + w.fk_off; sp.fk_bh_stride = g.N * g.Dp;
             sp.fkp = nullptr; sp.fkp_bh_stride = 0;
         }
+        sp.items_per_bh = state_items_per_bh(sp);
         hipError_t e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         if ((e = prof_mark(1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
         ScanParams cp{};
-        cp.partial = sp.partial; cp.init = nullptr; cp.state_out = nullptr;
+        cp.partial = sp.partial; cp.part = state_part(sp); cp.init = nullptr; cp.state_out = nullptr;
         cp.s_hi = ws + w.shi_off; cp.s_lo = ws + w.slo_off; cp.z = (float*)(ws + w.z_off);
         cp.s_chunk_stride = (long long)g.d * g.Dp; cp.s_bh_stride = (long long)g.C * g.d * g.Dp;
         cp.z_chunk_stride = g.Dp; cp.z_bh_stride = (long long)g.C * g.Dp;
@@ -529,10 +538,11 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         sp.n_blocks = w.U; sp.sub_rows = w.split.sub_rows; sp.n_sub = w.split.n_sub;
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi; sp.mode = mode; sp.F = g.F;
         sp.partial = (float*)(ws + w.part_off);
+        sp.items_per_bh = state_items_per_bh(sp);
         e = bf ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         ScanParams cp{};
-        cp.partial = sp.partial;
+        cp.partial = sp.partial; cp.part = state_part(sp);
         cp.s_hi = ws + w.shi_off; cp.s_lo = ws + w.slo_off; cp.t_hi = ws + w.thi_off; cp.t_lo = ws + w.tlo_off;
         cp.z = (float*)(ws + w.z_off);
         cp.s_chunk_stride = (long long)g.d * g.Dp; cp.s_bh_stride = (long long)g.C * g.d * g.Dp;
@@ -547,10 +557,11 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         gp.n_blocks = w.GU; gp.sub_rows = w.gsplit.sub_rows; gp.n_sub = w.gsplit.n_sub;
         gp.row_lse = lse; gp.row_d = bp.dsum;
         gp.partial = (float*)(ws + w.gpart_off);
+        gp.items_per_bh = state_items_per_bh(gp);
         e = bf ? launch_state_bf16(gp, s) : launch_state_f32(gp, s);
         if (e != hipSuccess) return hip_fail(e, "gradient-state launch");
         ScanParams gc = cp;
-        gc.partial = gp.partial; gc.U = w.GU; gc.n_sub = w.gsplit.n_sub;
+        gc.partial = gp.partial; gc.part = state_part(gp); gc.U = w.GU; gc.n_sub = w.gsplit.n_sub;
         gc.s_hi = ws + w.ghi_off; gc.s_lo = ws + w.glo_off; gc.t_hi = ws + w.gthi_off; gc.t_lo = ws + w.gtlo_off;
         gc.z = (float*)(ws + w.gz_off);
         gc.s_bh_stride = (long long)w.gslots * g.d * g.Dp; gc.z_bh_stride = (long long)w.gslots * g.Dp;
@@ -776,10 +787,11 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
             sp.fk = base + L.fk_off; sp.fk_bh_stride = n * g.Dp;
             sp.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; sp.fkp_bh_stride = (long long)g.To * g.HW * g.Dp;
         }
+        sp.items_per_bh = state_items_per_bh(sp);
         e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         ScanParams cp{};
-        cp.partial = sp.partial;
+        cp.partial = sp.partial; cp.part = state_part(sp);
         cp.init = nonempty ? (const float*)(base + L.S_off) : nullptr;
         cp.state_out = (float*)(base + L.S_off);
         cp.s_hi = base + L.shi_off; cp.s_lo = base + L.slo_off; cp.z = (float*)(base + L.z_off);

@@ -157,22 +157,18 @@ __global__ __launch_bounds__(256) void state_f32_kernel(StateParams p) {
     __shared__ float Zw[BN];
 
     const int tid = threadIdx.x;
-    const int blk = blockIdx.x;
-    const int per_bh = p.n_blocks * p.n_sub;
-    const int bh = blk / per_bh;
-    const int rem = blk - bh * per_bh;
-    const int u = rem / p.n_sub;
-    const int sub = rem - u * p.n_sub;
-    int e0, e1;
-    if (p.stream_rows > 0) {
-        e0 = 0;
-        e1 = p.stream_rows;
-    } else {
-        int fa, fb;
-        state_block_frames(p.mode, u, p.Tc, p.To, p.F, fa, fb);
-        e0 = fa * p.HW;
-        e1 = fb * p.HW;
+    // block -> (bh, u, sub), as in the bf16 kernel
+    const int bh = blockIdx.x / p.items_per_bh;
+    int sub = blockIdx.x - bh * p.items_per_bh;
+    const BlockPart part = state_part(p);
+    int u = 0;
+    for (; u < p.n_blocks - 1; ++u) {
+        const int n = part_block_subs(part, u);
+        if (sub < n) break;
+        sub -= n;
     }
+    int e0, e1;
+    part_block_rows(part, u, e0, e1);
     const int j0 = e0 + sub * p.sub_rows;
     const int j1 = min(j0 + p.sub_rows, e1);
     float* outp = p.partial + ((long long)(bh * p.n_blocks + u) * p.n_sub + sub) * (SE + DP);
@@ -266,7 +262,7 @@ hipError_t launch_local_d(const LocalParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_state_d(const StateParams& p, hipStream_t s) {
-    const int blocks = p.BH * p.n_blocks * p.n_sub;
+    const int blocks = p.BH * p.items_per_bh;
     if (blocks <= 0) return hipSuccess;
     switch (p.phi) {
     case kPhiElu1:

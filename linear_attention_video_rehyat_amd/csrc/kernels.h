@@ -162,7 +162,8 @@ struct StateParams {
     int HW, Tc, To;                   // delta block u covers frames [max(uTc-To,0), max((u+1)Tc-To,0))
     int n_blocks;                     // U: number of delta blocks
     int sub_rows;                     // key rows per sub-block
-    int n_sub;                        // sub-blocks per delta block (max over blocks)
+    int n_sub;                        // sub-blocks per delta block (max over blocks): the partial stride
+    int items_per_bh;                 // workgroups per (b, h): the sub-blocks of all blocks
     int stream_rows;                  // streaming: rows of [prev | chunk] to fold (U = 1); 0 in fwd
     int BH, d, phi;
     int mode, F;                      // block partition (BlockMode) and frames of the clip
@@ -176,10 +177,41 @@ struct StateParams {
     const float* row_lse; const float* row_d;
 };
 
+// The blocks of a state partition and their sub-blocks: block u covers rows
+// [e0, e1) (a single block of stream_rows rows in a streaming fold) and is
+// split into sub-blocks of sub_rows rows, one workgroup and one partial sum
+// each; an empty block has none (its sum is zero).
+struct BlockPart {
+    int mode, HW, Tc, To, F, stream_rows, sub_rows;
+};
+
+__host__ __device__ inline BlockPart state_part(const StateParams& p) {
+    return BlockPart{p.mode, p.HW, p.Tc, p.To, p.F, p.stream_rows, p.sub_rows};
+}
+
+__host__ __device__ inline void part_block_rows(const BlockPart& b, int u, int& e0, int& e1) {
+    if (b.stream_rows > 0) {
+        e0 = 0;
+        e1 = b.stream_rows;
+        return;
+    }
+    int fa, fb;
+    state_block_frames(b.mode, u, b.Tc, b.To, b.F, fa, fb);
+    e0 = fa * b.HW;
+    e1 = fb * b.HW;
+}
+
+__host__ __device__ inline int part_block_subs(const BlockPart& b, int u) {
+    int e0, e1;
+    part_block_rows(b, u, e0, e1);
+    return e1 > e0 ? (e1 - e0 + b.sub_rows - 1) / b.sub_rows : 0;
+}
+
 // Scan: X_0 = init (or 0); X_{u+1} = X_u + sum_p partial[u][p].  Writes the
 // prepared form of X_t for t in [t_first, U] and, if state_out, X_U in fp32.
 struct ScanParams {
-    const float* partial;             // [BH][U][n_sub][E]
+    const float* partial;             // [BH][U][n_sub][E], block u in its first part_block_subs(u) slots
+    BlockPart part;                   // the blocks the partial sums were made over
     const float* init;                // [BH][E] or null
     float* state_out;                 // [BH][E] or null (may alias init)
     void* s_hi; void* s_lo;           // prepared S^T per (bh, t) (bf16 hi/lo, or fp32 in s_hi)

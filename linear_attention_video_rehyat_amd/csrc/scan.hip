@@ -68,13 +68,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
     };
     // the sub-blocks' loads of a block sum are issued together (up to 4)
     auto block_sum = [&](int u) {
+        const int n = part_block_subs(p.part, u);
         f32x4 d[4];
 #pragma unroll
         for (int sp = 0; sp < 4; ++sp)
-            d[sp] = sp < p.n_sub ? *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+            d[sp] = sp < n ? *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 b = d[0] + d[1] + d[2] + d[3];
-        for (int sp = 4; sp < p.n_sub; ++sp) b += *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
+        for (int sp = 4; sp < n; ++sp) b += *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride);
         return b;
     };
     if (p.mode == kChunkRows) {
@@ -139,11 +139,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
     if (p.U <= MAXU && p.n_sub <= MAXS) {
         f32x4 d[MAXU][MAXS];
 #pragma unroll
-        for (int u = 0; u < MAXU; ++u)
+        for (int u = 0; u < MAXU; ++u) {
+            const int n = u < p.U ? part_block_subs(p.part, u) : 0;
 #pragma unroll
             for (int sp = 0; sp < MAXS; ++sp)
-                d[u][sp] = u < p.U && sp < p.n_sub ? *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride)
-                                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+                d[u][sp] = sp < n ? *(const f32x4*)(part + ((long long)u * p.n_sub + sp) * pstride)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int u = 0; u < MAXU; ++u) {
             if (u >= p.U) break;
@@ -163,9 +165,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             d[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (u0 + i < p.U)
-                for (int sp = 0; sp < p.n_sub; ++sp)
-                    d[i] += *(const f32x4*)(part + ((long long)(u0 + i) * p.n_sub + sp) * pstride);
+            if (u0 + i < p.U) d[i] = block_sum(u0 + i);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -116,24 +116,20 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
     const int nt0 = wave % (NT >= NW ? NW : NT);      // first feature tile of the wave
     const int kpart = wave / (NT >= NW ? NW : NT);    // which share of the 16-key steps
 
-    // block -> (bh, u, sub)
+    // block -> (bh, u, sub): the sub-blocks of a (b, h), block by block (only
+    // the workgroups with work are launched)
     const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
-    const int per_bh = p.n_blocks * p.n_sub;
-    const int bh = item / per_bh;
-    const int rem = item - bh * per_bh;
-    const int u = rem / p.n_sub;
-    const int sub = rem - u * p.n_sub;
-
-    int e0, e1;  // virtual key rows of the delta block
-    if (p.stream_rows > 0) {
-        e0 = 0;
-        e1 = p.stream_rows;
-    } else {
-        int fa, fb;
-        state_block_frames(p.mode, u, p.Tc, p.To, p.F, fa, fb);
-        e0 = fa * p.HW;
-        e1 = fb * p.HW;
+    const int bh = item / p.items_per_bh;
+    int sub = item - bh * p.items_per_bh;
+    const BlockPart part = state_part(p);
+    int u = 0;
+    for (; u < p.n_blocks - 1; ++u) {
+        const int n = part_block_subs(part, u);
+        if (sub < n) break;
+        sub -= n;
     }
+    int e0, e1;  // virtual key rows of the block
+    part_block_rows(part, u, e0, e1);
     const int j0 = e0 + sub * p.sub_rows;
     const int j1 = min(j0 + p.sub_rows, e1);
     const int nkeys = max(j1 - j0, 0);
@@ -341,7 +337,7 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
 
 template <int D>
 hipError_t launch_d(const StateParams& p, hipStream_t s) {
-    const long long blocks = (long long)p.BH * p.n_blocks * p.n_sub;
+    const long long blocks = (long long)p.BH * p.items_per_bh;
     if (blocks <= 0) return hipSuccess;
     switch (p.phi) {
     case kPhiElu1:
