@@ -109,6 +109,48 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
         }
         return;
     }
+    if (p.mode == kBidirectional && p.U <= 16 && p.C <= 8 && p.n_sub <= 2) {
+        // the same sums as below from block sums held in registers: every
+        // load is issued at once (U <= 16 blocks of at most 2 sub-blocks)
+        constexpr int MB = 16, MC = 8;
+        f32x4 bs[MB];
+#pragma unroll
+        for (int k = 0; k < MB; ++k) {
+            const int n = k < p.U ? part_block_subs(p.part, k) : 0;
+            const f32x4 a = n > 0 ? *(const f32x4*)(part + ((long long)k * p.n_sub) * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 b = n > 1 ? *(const f32x4*)(part + ((long long)k * p.n_sub + 1) * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+            bs[k] = a + b + f32x4{0.f, 0.f, 0.f, 0.f} + f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // suffix Y_{2t+3} for every chunk (zero past the last block)
+        f32x4 ys[MC];
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < MC; ++t) ys[t] = y;
+#pragma unroll
+        for (int k = MB - 1; k >= 0; --k) {
+            if (k >= p.U) continue;
+            y += bs[k];
+#pragma unroll
+            for (int t = 0; t < MC; ++t)
+                if (k >= 3 && (k & 1) && (k - 3) / 2 == t && t < p.C) ys[t] = y;
+        }
+        // prefix sums, forwards; chunk t adds the blocks before max(2(t-q), 0)
+        int k0 = 0;
+#pragma unroll
+        for (int t = 0; t < MC; ++t) {
+            if (t >= p.C) break;
+            const int pk = max(2 * (t - p.q), 0);
+#pragma unroll
+            for (int k = 0; k < MB; ++k)
+                if (k >= k0 && k < pk) x += bs[k];
+            k0 = max(k0, pk);
+            const f32x4 keep = x;
+            x += ys[t];
+            emit(t);
+            x = keep;
+        }
+        return;
+    }
     if (p.mode == kBidirectional) {
         // suffix sums Y_k = sum of blocks k.. U-1, backwards; chunk t needs
         // Y_{2t+3} (zero past the last block).  Each thread keeps its own 4
