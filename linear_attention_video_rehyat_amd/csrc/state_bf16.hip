@@ -96,14 +96,16 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
     constexpr int DT = D / 32;
     constexpr int C = D / 8;
     constexpr int KTILE = BN * KW;                    // elements of the K tile
-    constexpr int STAGE = KTILE + BN * D;             // K tile, then the V tile
-    constexpr int NLD = STAGE * 2 / 1024;             // 1 KB load instructions per stage
+    constexpr int GROWS = GRAD ? 4 * BN : 0;          // GRAD: the tile's lse, then its dsum (fp32)
+    constexpr int STAGE = KTILE + BN * D + GROWS;     // K tile, V tile, per-row values
+    constexpr int NLD = (KTILE + BN * D) * 2 / 1024;  // 1 KB load instructions per stage
     constexpr int OPW = NLD / NW;                     // per wave and stage
     constexpr int KSTEPS = BN / 16;
     static_assert(NT % NW == 0 || NW % NT == 0, "feature tiles must split evenly over the waves");
     static_assert(NLD % NW == 0, "tile loads must split evenly over the waves");
     static_assert(KSTEPS % SPLIT == 0, "16-key steps must split evenly over the waves sharing a tile");
     static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
+    static_assert(!GRAD || BN == 64, "one 4-byte-per-lane load carries a tile's lse (and one its dsum)");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem_raw[NS * STAGE];
     lds_u16* const smem = (lds_u16*)smem_raw;
@@ -150,11 +152,22 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, clip_rows * rb, 0x00020000);
     const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc((void*)kpb, (short)0, prev_end * krb, 0x00020000);
     const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc((void*)vpb, (short)0, prev_end * rb, 0x00020000);
+    // GRAD: rows are the clip's query rows (no overlap segment); waves 0 and 1
+    // also bring the tile's lse and dsum into the stage, through the same
+    // asynchronous path, so the per-row values never stall the MFMA loop
+    const bool grow_wave = GRAD && wave < 2;
+    __amdgpu_buffer_rsrc_t grs = krs;
+    if constexpr (GRAD) {
+        const float* g = (wave == 0 ? p.row_lse : p.row_d) + bh * (p.bh_stride / D);
+        grs = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, e1 * 4, 0x00020000);
+    }
     auto load_tile = [&](lds_u16* base, int t) {
         state_load_tile<D, KW, BN, NW, OPW>(base, wave, lane, j0 + t * BN, prev_rows, krs, vrs, kprs, vprs);
+        if (grow_wave) {
+            auto* lds = (__attribute__((address_space(3))) void*)(base + KTILE + BN * D + 2 * BN * wave);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, lds, 4, (j0 + t * BN + lane) * 4, 0, 0, 0);
+        }
     };
-    const float* glse = GRAD ? p.row_lse + bh * (p.bh_stride / D) : nullptr;
-    const float* gdsum = GRAD ? p.row_d + bh * (p.bh_stride / D) : nullptr;
 
     // transposing-read addressing (see lds_read_tr): for its column, lane
     // (half h) receives keys 4h..4h+3 of the first read and 8+4h..8+4h+3 of
@@ -205,11 +218,17 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
             const int kbase = t * BN + 16 * ks + 4 * h;  // key of element 0 (elements 4..7: +8)
             float gc[GRAD ? 8 : 1], gd[GRAD ? 8 : 1];  // per-row scale and z weight (backward)
             if constexpr (GRAD) {
+                // the stage's lse (BN floats), then dsum; rows past the block read as zero
+                typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+                const lds_f32x4* gv = (const lds_f32x4*)(Vs + BN * D);
+                const f32x4 l0 = gv[4 * ks + h], l1 = gv[4 * ks + h + 2];
+                const f32x4 d0 = gv[BN / 4 + 4 * ks + h], d1 = gv[BN / 4 + 4 * ks + h + 2];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = j0 + min(kbase + (e < 4 ? e : e + 4), nkeys - 1);  // clip row, clamped
-                    gc[e] = __expf(-glse[r]);
-                    gd[e] = gdsum[r];
+                for (int e = 0; e < 4; ++e) {
+                    gc[e] = __expf(-l0[e]);
+                    gc[e + 4] = __expf(-l1[e]);
+                    gd[e] = d0[e];
+                    gd[e + 4] = d1[e];
                 }
             }
             if constexpr (FEAT) {
@@ -286,9 +305,15 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
         // own loads of tile t have landed (later tiles may be in flight), then
         // every wave's have, and every wave is done with the slot refilled next
         const int ahead = min(NS - 2, ntiles - 1 - t);
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
-        else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        if (GRAD && grow_wave) {  // one more load per stage
+            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW + 2));
+            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW + 1));
+            else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        } else {
+            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
+            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
+            else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        }
         lds_barrier();
         iteration(t, smem + ((t + NS - 1) % NS) * STAGE, smem + (t % NS) * STAGE);
     }
