@@ -21,6 +21,8 @@
 // ahead; rows are stored unpadded with an XOR swizzle of their 16-byte chunks
 // so that both the K fragment reads and the transposing V reads are free of
 // bank conflicts.
+#include <type_traits>
+
 #include "local_common.h"
 
 namespace rehyat {
@@ -197,7 +199,10 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     // S^T(tile) = K Q^T (lane holds query lq, keys 32kt + (r/4)*8 + 4h + r%4),
     // then the online softmax -> P(tile), log2 domain; the running max is only
     // moved when a new score exceeds it by more than kRescaleThreshold
-    auto scores_softmax = [&](int it, const lds_u16* Ks) {
+    // TAIL: the window's last tile (only there are keys past the window end
+    // masked; the other tiles carry no per-score test at all)
+    auto scores_softmax = [&](auto tail, int it, const lds_u16* Ks) {
+        constexpr bool TAIL = decltype(tail)::value;
         f32x16 sacc[QB][KT];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, QB * AH, 0);
         }
-        if ((it + 1) * BN > nkeys) {  // keys past the window end (last tile only)
+        if (TAIL) {  // keys past the window end
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     // waves whose query rows all lie past the chunk end (in the chunk's last,
     // partial tile) only take their share of the loads and the barriers
     const bool active = q_start + wave * QB * 32 < q_end;
-    auto iteration = [&](int it, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
+    auto iteration = [&](auto tail, int it, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
         if (it + PF < ntiles)
             issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(fill, wave, it + PF, p.prev_rows, seg_shift, rb, op_row,
                                                            op_c16, krs, vrs, kprs, vprs);
@@ -315,11 +320,11 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
             if (S_ONE_SLOT) issue_state_dma<D, DP, NW>(fill + SPART, wave, lane, slo);
         }
         if (active) {
-            scores_softmax(it, cur);
+            scores_softmax(tail, it, cur);
             pv(cur + KTILE);
         }
     };
-    for (int it = 0; it < ntiles; ++it) {
+    auto step = [&](auto tail, int it) {
         // own loads of tile `it` have landed (tiles it+1 .. it+PF-1 may still be
         // in flight), then every wave's have, and every wave is done with the
         // slot refilled next
@@ -328,8 +333,12 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
         else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         lds_barrier();
-        iteration(it, smem + ((it + PF) % STAGES) * STAGE, smem + (it % STAGES) * STAGE);
-    }
+        iteration(tail, it, smem + ((it + PF) % STAGES) * STAGE, smem + (it % STAGES) * STAGE);
+    };
+    // the last tile, the only one that can be partial, is peeled off the loop:
+    // its key mask then adds no instructions (nor live registers) to the loop
+    for (int it = 0; it < ntiles - 1; ++it) step(std::false_type{}, it);
+    if (ntiles > 0) step(std::true_type{}, ntiles - 1);
 
     // ---------------------------------------------------------------- epilogue
     const lds_u16* s_lds = nullptr;
