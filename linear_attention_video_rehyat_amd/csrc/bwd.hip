@@ -593,8 +593,10 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dqt[dt] = f32x16{};
 
-    if (ntiles > 0) load_tile(0, 0);
-    for (int it = 0; it < ntiles; ++it) {
+    // one key tile; TAIL: the window's last tile, the only one whose keys can
+    // run past the window end (the others carry no key test)
+    auto tile_step = [&](auto tail, int it) {
+        constexpr bool TAIL = decltype(tail)::value;
         const int buf = it & 1;
         __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         lds_barrier();
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int kr = it * BN + 32 * ks + 8 * j + 4 * h + i;
-                    const float pe = kr < nkeys ? __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - lse2) : 0.0f;
+                    const float pe = !TAIL || kr < nkeys ? __builtin_amdgcn_exp2f(sacc[4 * j + i] * kLog2e - lse2) : 0.0f;
                     dv[i] = pe * (pacc[4 * j + i] - dsum);
                 }
                 dw[j >> 1][2 * (j & 1)] = pack2_bf16(dv[0], dv[1]);
@@ -644,7 +646,10 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
                 }
             }
         }
-    }
+    };
+    if (ntiles > 0) load_tile(0, 0);
+    for (int it = 0; it < ntiles - 1; ++it) tile_step(std::false_type{}, it);
+    if (ntiles > 0) tile_step(std::true_type{}, ntiles - 1);
 
     // ---- linear branch: dphi(q) = e^{-lse} (S_t dy - D z_t)
     if constexpr (PHI != kPhiNone) {
