@@ -17,8 +17,8 @@
 // between the two 32-lane halves.  P^T then feeds O^T += V^T P^T directly from
 // registers; V^T fragments come from the row-major V tile in LDS through the
 // transposing LDS read.  K/V tiles of BN keys stream into a ring of LDS stages
-// by direct global->LDS buffer loads (no register staging), issued two tiles
-// ahead; rows are stored unpadded with an XOR swizzle of their 16-byte chunks
+// by direct global->LDS buffer loads (no register staging), issued STAGES - 1
+// tiles ahead (one in the default two-stage ring); rows are stored unpadded with an XOR swizzle of their 16-byte chunks
 // so that both the K fragment reads and the transposing V reads are free of
 // bank conflicts.
 #include <type_traits>
