@@ -62,6 +62,7 @@ SMALL = [
     (1, 1, 6, 300, 128, 4, 2),
     (1, 3, 4, 45, 32, 1, 2),
     (1, 1, 3, 17, 128, 5, 1),     # one chunk longer than the clip: plain softmax
+    (1, 2, 5, 128, 128, 1, 1),    # windows of whole key tiles: the last tile is a full one
 ]
 
 

@@ -66,6 +66,7 @@ SMALL = [
     (2, 1, 6, 33, 64, 3, 0),
     (1, 2, 4, 45, 32, 1, 2),
     (1, 1, 3, 40, 128, 5, 1),     # one chunk: plain softmax attention
+    (1, 2, 5, 128, 128, 1, 1),    # windows of whole key tiles: the last tile is a full one
 ]
 
 
