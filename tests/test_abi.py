@@ -144,3 +144,25 @@ def test_local_work_order_is_a_permutation(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "0 violations" in run.stdout
+
+
+def test_key_block_partition(tmp_path):
+    """The key blocks of the state pass and the scan (kernels.h): each chunk's
+    linear set is exactly the keys outside its softmax window, recurrent and
+    bidirectional (ReHyAt §3.2, §3.3), assembled from whole blocks; sub-blocks
+    cover every block's rows; the state kernel's workgroup decode visits every
+    (block, sub-block) once.  Host-side build with hipcc, run on the CPU."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    src = os.path.join(ROOT, "tests", "native", "block_partition_check.cpp")
+    exe = str(tmp_path / "block_partition_check")
+    csrc = os.path.join(ROOT, "linear_attention_video_rehyat_amd", "csrc")
+    build = subprocess.run([hipcc, "-O1", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", f"-I{csrc}",
+                            src, "-o", exe], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert " 0 violations" in run.stdout
