@@ -573,6 +573,16 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         bp.gt_hi = ws + w.gthi_off; bp.gt_lo = ws + w.gtlo_off; bp.gz = (const float*)(ws + w.gz_off);
         bp.s_stride = (long long)g.d * g.Dp; bp.z_stride = g.Dp;
     }
+    if (bf) {
+        // dq's work items have the local kernel's shape (the windows of chunk 0
+        // are shorter): the same simulated choice of dispatch order
+        int tpc = 0, bn = 0;
+        dq_launch_shape(bp, tpc, bn);
+        LocalParams lp{};
+        lp.BH = bp.BH; lp.n_chunks = bp.C; lp.tiles_per_chunk = tpc;
+        lp.F = bp.F; lp.Tc = bp.Tc; lp.To = bp.To; lp.HW = bp.HW;
+        bp.dq_lpt = choose_lpt_order(lp, bp.BH * bp.C * tpc, bn);
+    }
     e = bf ? launch_bwd_bf16(bp, s) : launch_bwd_f32(bp, s);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return REHYAT_OK;

@@ -529,7 +529,12 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, lq = lane & 31;
-    const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    // items (b, h, chunk, query tile) in the local kernel's order: each XCD owns
+    // a contiguous share, optionally taken longest window first
+    LocalParams wl{};
+    wl.F = p.F; wl.Tc = p.Tc; wl.To = p.To; wl.HW = p.HW;
+    wl.n_chunks = p.C; wl.tiles_per_chunk = tiles_per_chunk; wl.lpt_order = p.dq_lpt;
+    const int item = __builtin_amdgcn_readfirstlane(local_work_item(wl, blockIdx.x, gridDim.x, BN));
     const int per_bh = p.C * tiles_per_chunk;
     const int bh = item / per_bh;
     const int rem = item - bh * per_bh;
@@ -934,6 +939,11 @@ hipError_t launch_bwd_dsum(const BwdParams& p, float* dsum, bool bf16, hipStream
     if (!bf16) return dsum_typed<float, float>(p, (const float*)p.out, dsum, s);
     if (p.out_f32) return dsum_typed<uint16_t, float>(p, p.out_f32, dsum, s);
     return dsum_typed<uint16_t, uint16_t>(p, (const uint16_t*)p.out, dsum, s);
+}
+
+void dq_launch_shape(const BwdParams& p, int& tiles_per_chunk, int& key_tile) {
+    tiles_per_chunk = dq_tiles_per_chunk(p, kBwdQueries);
+    key_tile = kBwdKTile;
 }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {

@@ -250,6 +250,7 @@ struct BwdParams {
     int lin;                          // the linear branch is active (some chunk has a linear set)
     int mode;                         // kCausal or kBidirectional (then: G per bidirectional block,
                                       // 2C+1 slots, and every chunk has a linear set)
+    int dq_lpt;                       // dq workgroups: each XCD's items longest first (local_work_item)
 };
 
 // Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot
@@ -293,6 +294,9 @@ hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s);
 hipError_t launch_phi_mlp_bf16(const MlpParams& p, hipStream_t s);
 hipError_t launch_bwd_dsum(const BwdParams& p, float* dsum, bool bf16, hipStream_t s);  // dsum = rowwise dy . out
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);   // dq, dk, dv
+// The bf16 dq kernel's work items: query tiles per chunk and keys per tile (for
+// the host's choice of dispatch order).
+void dq_launch_shape(const BwdParams& p, int& tiles_per_chunk, int& key_tile);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_phi_mlp_f32(const MlpParams& p, hipStream_t s);
 bool phi_mlp_hidden_ok(int hidden);  // hidden widths the MLP kernels are built for
