@@ -15,8 +15,8 @@
  *   y   = (a^S + a^L) / (n^S + n^L)                          (§3.2, first equation)
  *
  * The linear sums over T^L_t are carried from chunk to chunk as the state
- * (S = sum phi(k) v^T, z = sum phi(k)) of the chunk-wise RNN form (§3.3; the
- * abstract's "chunk-wise recurrent reformulation and constant memory usage").
+ * (S = sum phi(k) v^T, z = sum phi(k)) of the chunk-wise RNN form, whose memory
+ * does not grow with the length of the video (abstract and §3.3).
  *
  * Conventions shared by every entry point
  *   - Tensors are device pointers to contiguous [B][H][N][head_dim] arrays,
@@ -32,7 +32,20 @@
  *     null stream).  Arguments are validated on the host before any GPU work is
  *     queued; on failure nothing is queued, the status is returned and
  *     rehyat_last_error() describes it.  Errors raised by the HIP runtime while
- *     queueing map to REHYAT_EHIP.  No call aborts or throws across the ABI.
+ *     queueing map to REHYAT_EHIP; the kernels already queued by that call may
+ *     then have run, and its outputs are undefined.  No call aborts or throws
+ *     across the ABI.
+ *   - Streams and threads: the workspace of the whole-clip calls comes from an
+ *     arena per (device, stream), so calls on different streams may run
+ *     concurrently.  Calls on one stream from several threads are serialised
+ *     while they queue their launches (each call holds its arena until its last
+ *     launch is queued).  The arena of a stream lives until the process ends or
+ *     rehyat_workspace_release() frees it; release it before destroying a stream
+ *     that made calls.
+ *   - Sizes: the rows of one (b, h) are addressed with 32-bit byte offsets, so
+ *     frames * tokens_per_frame * (row bytes) must stay below 2^31, where a row
+ *     is head_dim elements (2 head_dim with the learned maps); larger clips are
+ *     rejected with REHYAT_EUNSUPPORTED (at head_dim 128 in bf16: 8,388,607 tokens).
  */
 #ifndef REHYAT_H
 #define REHYAT_H
@@ -67,8 +80,9 @@ typedef enum rehyat_dtype { REHYAT_F32 = 0, REHYAT_BF16 = 1 } rehyat_dtype;
  *   q, k, v : in,  [B][H][frames*tokens_per_frame][head_dim] bf16
  *   out     : out, same shape and dtype; must not alias q, k or v
  * A transient fp32 workspace (about ceil(F/T_c) * B * H * (D' head_dim + D') * 12 bytes)
- * comes from a per-device arena the library grows on demand and keeps for
- * the life of the process (REHYAT_ENOMEM if it cannot grow).  With
+ * comes from the arena of (current device, stream), which the library grows on
+ * demand and keeps until the process ends or rehyat_workspace_release()
+ * (REHYAT_ENOMEM if it cannot grow).  With
  * chunk_frames >= frames and REHYAT_PHI_NONE this is plain bidirectional
  * softmax attention (the dense comparison point).
  */
@@ -162,7 +176,10 @@ rehyat_status rehyat_step_state_init(rehyat_step_state* st, void* buf, size_t by
  * in the state's dtype, 1 <= frames <= chunk_frames.  Every call but the last
  * of a stream must pass frames == chunk_frames; then the concatenated outputs
  * equal rehyat_attn_fwd on the concatenated inputs.  Updates `st`.
- * Concurrent calls on one state are not allowed.
+ * Concurrent calls on one state are not allowed.  A step that returns
+ * REHYAT_EHIP leaves the host header unchanged, but the device buffer may
+ * already hold part of the chunk's update: restore a saved state (buffer and
+ * header) before continuing the stream.
  */
 rehyat_status rehyat_attn_step(rehyat_step_state* st, const void* q, const void* k, const void* v,
                                void* out, int frames, void* stream);
@@ -200,7 +217,7 @@ rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int
 
 /* Forward with the learned maps: the contract of rehyat_attn_fwd (causal != 0)
  * or rehyat_attn_fwd_bidir (causal == 0), in dtype, with phi(q) = phi_q(q) and
- * phi(k) = phi_k(k).  The per-device workspace also holds phi(q) and phi(k)
+ * phi(k) = phi_k(k).  The stream's workspace arena also holds phi(q) and phi(k)
  * (B H N 2 head_dim elements each). */
 rehyat_status rehyat_attn_fwd_mlp(const void* q, const void* k, const void* v, void* out, int dtype,
                                   int B, int H, int frames, int tokens_per_frame, int head_dim,
@@ -244,7 +261,7 @@ rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const v
  *   through the same cached sums as the forward: the forward states S_t, z_t,
  *   and their reverse-order counterpart, sums over the chunks whose linear set
  *   holds a key's block (later chunks; bidirectional: later and earlier ones)
- *   of e^{-lse} phi(q) dout^T.  Workspace comes from the forward's per-device arena.
+ *   of e^{-lse} phi(q) dout^T.  Workspace comes from the stream's arena.
  *   Deterministic: no atomics, fixed summation order.
  */
 rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -266,6 +283,25 @@ rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const
  * n_events must be 0 or 4.
  */
 rehyat_status rehyat_set_profile_events(void* const* events, int n_events);
+
+/*
+ * Waits for the work queued on `stream` (on the current device) and frees the
+ * workspace arena of that stream.  The next call on the stream allocates a new
+ * one.  Must not run concurrently with a call on the same stream.
+ */
+rehyat_status rehyat_workspace_release(void* stream);
+
+/*
+ * Test hook (fault injection).  Every HIP runtime call and kernel launch that
+ * an entry point makes counts as one HIP step, numbered from 0 per call on the
+ * calling thread.  rehyat_debug_inject_hip_error(n) arms the hook: the next
+ * call that reaches step n returns REHYAT_EHIP at that step without making
+ * the HIP call (so nothing after it is queued), and the hook disarms.  n < 0
+ * disarms it.  rehyat_debug_hip_steps() returns the number of HIP steps the
+ * last call on this thread made (or attempted).
+ */
+void rehyat_debug_inject_hip_error(int step);
+int rehyat_debug_hip_steps(void);
 
 /* Static description of a status code. */
 const char* rehyat_status_string(int status);

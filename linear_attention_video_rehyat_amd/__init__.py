@@ -16,7 +16,8 @@ import ctypes
 import os
 
 __all__ = ["RehyatError", "attn_fwd", "attn_fwd_partials", "attn_fwd_lse", "attn_bwd", "StepState",
-           "feature_map_id", "MlpWeights", "feature_mlp", "library_path", "load_library", "exported_symbols"]
+           "feature_map_id", "MlpWeights", "feature_mlp", "library_path", "load_library", "exported_symbols",
+           "workspace_release", "debug_inject_hip_error", "debug_hip_steps"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "librehyat.so")
@@ -32,6 +33,7 @@ exported_symbols = (
     "rehyat_step_state_bytes", "rehyat_step_state_init", "rehyat_attn_step",
     "rehyat_feature_mlp", "rehyat_attn_fwd_mlp", "rehyat_attn_fwd_mlp_partials", "rehyat_attn_step_mlp",
     "rehyat_attn_fwd_lse", "rehyat_attn_bwd",
+    "rehyat_workspace_release", "rehyat_debug_inject_hip_error", "rehyat_debug_hip_steps",
     "rehyat_set_profile_events", "rehyat_status_string", "rehyat_last_error", "rehyat_version",
 )
 
@@ -98,6 +100,12 @@ def load_library():
     lib.rehyat_attn_fwd_lse.restype = i
     lib.rehyat_attn_bwd.argtypes = [vp] * 10 + [i] * 10 + [vp]
     lib.rehyat_attn_bwd.restype = i
+    lib.rehyat_workspace_release.argtypes = [vp]
+    lib.rehyat_workspace_release.restype = i
+    lib.rehyat_debug_inject_hip_error.argtypes = [i]
+    lib.rehyat_debug_inject_hip_error.restype = None
+    lib.rehyat_debug_hip_steps.argtypes = []
+    lib.rehyat_debug_hip_steps.restype = i
     lib.rehyat_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     lib.rehyat_set_profile_events.restype = i
     lib.rehyat_status_string.argtypes = [i]
@@ -220,8 +228,8 @@ def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, fe
         raise RehyatError(1, f"N={N} != frames*tokens_per_frame={frames * tokens_per_frame}")
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise RehyatError(1, "out must match q")
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise RehyatError(1, "out must be a contiguous GPU tensor matching q")
     pair = _mlp_pair(feature_map)
     if pair is not None:
         _check(lib.rehyat_attn_fwd_mlp(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_id(q),
@@ -278,8 +286,13 @@ def attn_fwd_lse(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames
     B, H, N, d = q.shape
     if out is None:
         out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise RehyatError(1, "out must be a contiguous GPU tensor matching q")
     if lse is None:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or not lse.is_cuda):
+        raise RehyatError(1, "lse must be a contiguous float32 [B, H, N] GPU tensor")
     want32 = out_f32 is not None and out_f32 is not False
     if out_f32 is True:
         out_f32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -304,6 +317,9 @@ def attn_bwd(q, k, v, out, lse, dout, frames, tokens_per_frame, chunk_frames, ov
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise RehyatError(1, "lse must be a contiguous float32 [B, H, N] tensor")
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise RehyatError(1, "gradients must be contiguous GPU tensors matching q")
     if out_f32 is not None and (out_f32.shape != q.shape or out_f32.dtype != torch.float32
                                 or not out_f32.is_contiguous()):
         raise RehyatError(1, "out_f32 must be a contiguous float32 tensor shaped like q")
@@ -313,6 +329,22 @@ def attn_bwd(q, k, v, out, lse, dout, frames, tokens_per_frame, chunk_frames, ov
                                B, H, frames, tokens_per_frame, d, chunk_frames, overlap_frames,
                                feature_map_id(feature_map), 1 if causal else 0, _stream_handle(stream)))
     return dq, dk, dv
+
+
+def workspace_release(stream=None):
+    """Wait for the stream's queued work and free its workspace arena."""
+    _check(load_library().rehyat_workspace_release(_stream_handle(stream)))
+
+
+def debug_inject_hip_error(step: int):
+    """Test hook: the next call that reaches HIP step ``step`` fails there with
+    REHYAT_EHIP without making that HIP call; a negative step disarms."""
+    load_library().rehyat_debug_inject_hip_error(int(step))
+
+
+def debug_hip_steps() -> int:
+    """HIP steps (runtime calls and launches) of the last call on this thread."""
+    return int(load_library().rehyat_debug_hip_steps())
 
 
 def set_profile_events(events):
@@ -375,6 +407,8 @@ class StepState:
             raise RehyatError(1, f"chunk rows {n} not a multiple of tokens_per_frame {HW}")
         if out is None:
             out = torch.empty_like(q)
+        elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+            raise RehyatError(1, "out must be a contiguous GPU tensor matching the chunk")
         if self.mlp is not None:
             _check(lib.rehyat_attn_step_mlp(ctypes.byref(self._c), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                             out.data_ptr(), n // HW, self.mlp[0].check(q), self.mlp[1].check(k),

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <map>
+#include <memory>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -29,8 +30,35 @@ namespace {
 thread_local std::string g_last_error;
 thread_local hipEvent_t g_prof[4] = {nullptr, nullptr, nullptr, nullptr};
 
+// Fault injection (test hook, rehyat_debug_inject_hip_error): every HIP
+// runtime call and kernel launch an entry point makes is one "HIP step",
+// counted per call on the calling thread.  When armed, step g_inject_at of the
+// next call that reaches it fails with REHYAT_EHIP instead of being made; the
+// hook then disarms itself.
+thread_local int g_inject_at = -1;
+thread_local int g_steps = 0;
+thread_local bool g_injected = false;
+
+// Start of an entry point's GPU work: clear the last error and the step count.
+void begin_call() {
+    g_last_error.clear();
+    g_steps = 0;
+    g_injected = false;
+}
+
+template <class Fn>
+hipError_t hip_step(Fn&& fn) {
+    const int i = g_steps++;
+    if (i == g_inject_at) {
+        g_inject_at = -1;
+        g_injected = true;
+        return hipErrorLaunchFailure;
+    }
+    return fn();
+}
+
 hipError_t prof_mark(int i, hipStream_t s) {
-    return g_prof[i] ? hipEventRecord(g_prof[i], s) : hipSuccess;
+    return g_prof[i] ? hip_step([&] { return hipEventRecord(g_prof[i], s); }) : hipSuccess;
 }
 
 rehyat_status fail(rehyat_status st, const char* fmt, ...) {
@@ -44,6 +72,9 @@ rehyat_status fail(rehyat_status st, const char* fmt, ...) {
 }
 
 rehyat_status hip_fail(hipError_t e, const char* what) {
+    if (g_injected)
+        return fail(REHYAT_EHIP, "%s: injected failure at HIP step %d (rehyat_debug_inject_hip_error)", what,
+                    g_steps - 1);
     return fail(REHYAT_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -104,6 +135,14 @@ rehyat_status check_common(Geometry& g, int B, int H, int frames, int tpf, int d
         return fail(REHYAT_EUNSUPPORTED, "head_dim %d not supported for fp32 (16, 32, 64, 128)", d);
     const long long N = (long long)frames * tpf;
     if (N > (1LL << 30)) return fail(REHYAT_EINVAL, "frames*tokens_per_frame = %lld is too large", N);
+    // the kernels address the rows of one (b, h) through buffer resources with
+    // 32-bit byte offsets: every per-(b, h) extent (input rows, and the learned
+    // map's 2 head_dim-wide feature rows) must stay below 2^31 bytes
+    const long long row_bytes = (long long)(mlp ? 2 * d : d) * (dtype == REHYAT_BF16 ? 2 : 4);
+    if (N * row_bytes >= (1LL << 31))
+        return fail(REHYAT_EUNSUPPORTED,
+                    "frames*tokens_per_frame = %lld is too large: %lld bytes of rows per (b, h) exceed the "
+                    "2^31-byte extent the kernels address", N, N * row_bytes);
     const long long BH = (long long)B * H;
     if (BH > (1LL << 24)) return fail(REHYAT_EINVAL, "B*H = %lld is too large", BH);
     g.B = B; g.H = H; g.F = frames; g.HW = tpf; g.d = d; g.Tc = Tc; g.To = To; g.phi = phi; g.dtype = dtype;
@@ -180,40 +219,80 @@ int choose_lpt_order(const LocalParams& lp, int blocks, int bn) {
     return use;
 }
 
-// ---------------------------------------------------------------- workspace arena
+// ---------------------------------------------------------------- workspace arenas
+// One arena per (device, stream): calls queued on different streams never
+// share workspace, so they may run concurrently.  A lease holds its arena's
+// lock from the moment a call takes the workspace until the call's last launch
+// is queued; a concurrent call on the same stream from another thread waits
+// rather than growing (and freeing) the buffer under it.  Growing waits for the
+// stream's queued work, the only work that can still use the old buffer.
 struct Arena {
+    std::mutex mu;
     void* ptr = nullptr;
     size_t bytes = 0;
 };
-std::mutex g_arena_mu;
-std::vector<Arena> g_arenas;
+std::mutex g_arenas_mu;
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<Arena>> g_arenas;
 
-rehyat_status arena_get(size_t bytes, void** out) {
+struct ArenaLease {
+    std::unique_lock<std::mutex> lock;
+    char* ptr = nullptr;
+};
+
+rehyat_status arena_acquire(size_t bytes, hipStream_t s, ArenaLease& lease) {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    hipError_t e = hip_step([&] { return hipGetDevice(&dev); });
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    std::lock_guard<std::mutex> lock(g_arena_mu);
-    if ((int)g_arenas.size() <= dev) g_arenas.resize(dev + 1);
-    Arena& a = g_arenas[dev];
-    if (a.bytes < bytes) {
-        if (a.ptr) {
-            // earlier calls may still be using the old buffer
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            (void)hipFree(a.ptr);
-            a.ptr = nullptr;
-            a.bytes = 0;
+    Arena* a = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_arenas_mu);
+        std::unique_ptr<Arena>& slot = g_arenas[{dev, (uintptr_t)s}];
+        if (!slot) slot.reset(new Arena());
+        a = slot.get();
+    }
+    std::unique_lock<std::mutex> lock(a->mu);
+    if (a->bytes < bytes) {
+        if (a->ptr) {
+            e = hip_step([&] { return hipStreamSynchronize(s); });
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(a->ptr);
+            a->ptr = nullptr;
+            a->bytes = 0;
         }
-        size_t want = bytes + bytes / 4 + (1u << 20);
-        e = hipMalloc(&a.ptr, want);
+        const size_t want = bytes + bytes / 4 + (1u << 20);
+        e = hip_step([&] { return hipMalloc(&a->ptr, want); });
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            a.ptr = nullptr;
+            a->ptr = nullptr;
+            if (g_injected) return hip_fail(e, "hipMalloc");
             return fail(REHYAT_ENOMEM, "cannot allocate %zu bytes of workspace: %s", want, hipGetErrorString(e));
         }
-        a.bytes = want;
+        a->bytes = want;
     }
-    *out = a.ptr;
+    lease.ptr = (char*)a->ptr;
+    lease.lock = std::move(lock);
+    return REHYAT_OK;
+}
+
+// Waits for the stream's queued work and frees its arena on the current device.
+rehyat_status arena_release(hipStream_t s) {
+    int dev = 0;
+    hipError_t e = hip_step([&] { return hipGetDevice(&dev); });
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::unique_ptr<Arena> a;
+    {
+        std::lock_guard<std::mutex> lock(g_arenas_mu);
+        auto it = g_arenas.find({dev, (uintptr_t)s});
+        if (it == g_arenas.end()) return REHYAT_OK;
+        std::lock_guard<std::mutex> alock(it->second->mu);  // no call holds a lease on it now
+        a = std::move(it->second);
+        g_arenas.erase(it);
+    }
+    if (a->ptr) {
+        e = hip_step([&] { return hipStreamSynchronize(s); });
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        (void)hipFree(a->ptr);
+    }
     return REHYAT_OK;
 }
 
@@ -303,25 +382,28 @@ void mlp_rows(const Geometry& g, int mode, int& q0, int& k1) {
     k1 = (int)(std::max<long long>((long long)(g.C - 1) * g.Tc - g.To, 0) * g.HW);
 }
 
-rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g, int mode,
-                      float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s,
-                      const rehyat_mlp_weights* wq = nullptr, const rehyat_mlp_weights* wk = nullptr,
-                      float* lse = nullptr, float* out_f32 = nullptr) {
+// Bytes of workspace a whole-clip forward needs (0 when no chunk has a linear set).
+size_t fwd_workspace_bytes(const Geometry& g, int mode) {
+    return any_linear(g, mode) ? fwd_workspace(g, mode).total : 0;
+}
+
+// The launches of a whole-clip forward, with its workspace at `ws`
+// (fwd_workspace_bytes(g, mode) bytes; null when that is 0).
+rehyat_status run_fwd_ws(const void* q, const void* k, const void* v, void* out, const Geometry& g, int mode,
+                         float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s,
+                         const rehyat_mlp_weights* wq, const rehyat_mlp_weights* wk, float* lse, float* out_f32,
+                         char* ws) {
     const bool lin = any_linear(g, mode);
-    char* ws = nullptr;
     FwdWorkspace w{};
     hipError_t pe = prof_mark(0, s);
     if (pe != hipSuccess) return hip_fail(pe, "hipEventRecord");
     if (lin) {
         w = fwd_workspace(g, mode);
-        void* p = nullptr;
-        rehyat_status st = arena_get(w.total, &p);
-        if (st != REHYAT_OK) return st;
-        ws = (char*)p;
+        if (!ws) return fail(REHYAT_EINVAL, "internal: forward without its workspace");
         if (g.phi == REHYAT_PHI_MLP2) {
             int q0 = 0, k1 = 0;
             mlp_rows(g, mode, q0, k1);
-            hipError_t e = launch_mlp(g, wq, wk, q, ws + w.fq_off, g.N, q0, (int)g.N, k, ws + w.fk_off, g.N, 0, k1, s);
+            hipError_t e = hip_step([&] { return launch_mlp(g, wq, wk, q, ws + w.fq_off, g.N, q0, (int)g.N, k, ws + w.fk_off, g.N, 0, k1, s); });
             if (e != hipSuccess) return hip_fail(e, "feature-map launch");
         }
 
@@ -338,7 +420,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
             sp.fkp = nullptr; sp.fkp_bh_stride = 0;
         }
         sp.items_per_bh = state_items_per_bh(sp);
-        hipError_t e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
+        hipError_t e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s); });
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         if ((e = prof_mark(1, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
@@ -351,7 +433,7 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
         cp.t_first = mode == kBidirectional ? 0 : 1; cp.t_offset = 0; cp.f32_prep = g.dtype == REHYAT_F32;
         cp.mode = mode; cp.C = g.C; cp.q = g.To / g.Tc;
         cp.suffix = mode == kBidirectional ? (float*)(ws + w.suffix_off) : nullptr;
-        e = launch_scan(cp, s);
+        e = hip_step([&] { return launch_scan(cp, s); });
         if (e != hipSuccess) return hip_fail(e, "scan launch");
     } else {
         if ((pe = prof_mark(1, s)) != hipSuccess) return hip_fail(pe, "hipEventRecord");
@@ -383,10 +465,24 @@ rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, co
     lp.pm = pm; lp.pnt = pnt; lp.poS = poS; lp.poL = poL; lp.pnL = pnL;
     lp.lse = lse;
     lp.out_f32 = g.dtype == REHYAT_BF16 ? out_f32 : nullptr;
-    hipError_t e = g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s);
+    hipError_t e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s); });
     if (e != hipSuccess) return hip_fail(e, "local-attention launch");
     if ((e = prof_mark(3, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return REHYAT_OK;
+}
+
+// A whole-clip forward with its workspace from the stream's arena.
+rehyat_status run_fwd(const void* q, const void* k, const void* v, void* out, const Geometry& g, int mode,
+                      float* pm, float* pnt, float* poS, float* poL, float* pnL, hipStream_t s,
+                      const rehyat_mlp_weights* wq = nullptr, const rehyat_mlp_weights* wk = nullptr,
+                      float* lse = nullptr, float* out_f32 = nullptr) {
+    ArenaLease lease;
+    const size_t need = fwd_workspace_bytes(g, mode);
+    if (need) {
+        const rehyat_status st = arena_acquire(need, s, lease);
+        if (st != REHYAT_OK) return st;
+    }
+    return run_fwd_ws(q, k, v, out, g, mode, pm, pnt, poS, poL, pnL, s, wq, wk, lse, out_f32, lease.ptr);
 }
 
 // Weights of the learned query and key maps: present, 16-byte aligned, and a
@@ -421,7 +517,7 @@ rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, 
     const size_t bytes = (size_t)g.BH * g.N * g.d * g.elem;
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
         return fail(REHYAT_EINVAL, "out must not overlap q, k or v");
-    g_last_error.clear();
+    begin_call();
     return run_fwd(q, k, v, out, g, mode, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream, wq, wk);
 }
 
@@ -439,7 +535,7 @@ rehyat_status partials_entry(const void* q, const void* k, const void* v, int dt
     const void* ptrs[8] = {q, k, v, m, nt, o_s, o_l, n_l};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(REHYAT_EINVAL, "pointers must be 16-byte aligned");
-    g_last_error.clear();
+    begin_call();
     return run_fwd(q, k, v, nullptr, g, mode, m, nt, o_s, o_l, n_l, (hipStream_t)stream, wq, wk);
 }
 
@@ -511,15 +607,15 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         for (int b = a + 1; b < 3; ++b)
             if (overlaps(outs[a], bytes, outs[b], bytes)) return fail(REHYAT_EINVAL, "gradients must not overlap");
     }
-    g_last_error.clear();
+    begin_call();
     hipStream_t s = (hipStream_t)stream;
     const bool bf = g.dtype == REHYAT_BF16;
     const bool bidir = mode == kBidirectional;
     const bool lin = any_linear(g, mode);
     const BwdWorkspace w = bwd_workspace(g, mode);
-    void* wsp = nullptr;
-    if ((st = arena_get(w.total, &wsp)) != REHYAT_OK) return st;
-    char* ws = (char*)wsp;
+    ArenaLease lease;
+    if ((st = arena_acquire(w.total, s, lease)) != REHYAT_OK) return st;
+    char* ws = lease.ptr;
 
     BwdParams bp{};
     bp.q = q; bp.k = k; bp.v = v; bp.dy = dout; bp.out = out; bp.out_f32 = bf ? out_f32 : nullptr;
@@ -528,7 +624,7 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
     bp.bh_stride = g.N * g.d;
     bp.N = (int)g.N; bp.HW = g.HW; bp.F = g.F; bp.Tc = g.Tc; bp.To = g.To; bp.C = g.C; bp.BH = g.BH;
     bp.d = g.d; bp.phi = lin ? g.phi : REHYAT_PHI_NONE; bp.lin = lin ? 1 : 0; bp.mode = mode;
-    hipError_t e = launch_bwd_dsum(bp, (float*)(ws + w.dsum_off), bf, s);
+    hipError_t e = hip_step([&] { return launch_bwd_dsum(bp, (float*)(ws + w.dsum_off), bf, s); });
     if (e != hipSuccess) return hip_fail(e, "backward dsum launch");
     if (lin) {
         // the forward's states S_t, z_t (both layouts of S_t)
@@ -539,7 +635,7 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         sp.BH = g.BH; sp.d = g.d; sp.phi = g.phi; sp.mode = mode; sp.F = g.F;
         sp.partial = (float*)(ws + w.part_off);
         sp.items_per_bh = state_items_per_bh(sp);
-        e = bf ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
+        e = hip_step([&] { return bf ? launch_state_bf16(sp, s) : launch_state_f32(sp, s); });
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         ScanParams cp{};
         cp.partial = sp.partial; cp.part = state_part(sp);
@@ -550,7 +646,7 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         cp.U = w.U; cp.n_sub = w.split.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
         cp.t_first = bidir ? 0 : 1; cp.t_offset = 0; cp.f32_prep = !bf; cp.mode = mode; cp.C = g.C;
         cp.q = g.To / g.Tc; cp.suffix = bidir ? (float*)(ws + w.suffix_off) : nullptr;
-        if ((e = launch_scan(cp, s)) != hipSuccess) return hip_fail(e, "scan launch");
+        if ((e = hip_step([&] { return launch_scan(cp, s); })) != hipSuccess) return hip_fail(e, "scan launch");
         // gradient sums per chunk (rows: the chunk's queries, second operand dy)
         StateParams gp = sp;
         gp.k = q; gp.v = dout; gp.mode = bidir ? kChunkRowsAll : kChunkRows;
@@ -558,7 +654,7 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         gp.row_lse = lse; gp.row_d = bp.dsum;
         gp.partial = (float*)(ws + w.gpart_off);
         gp.items_per_bh = state_items_per_bh(gp);
-        e = bf ? launch_state_bf16(gp, s) : launch_state_f32(gp, s);
+        e = hip_step([&] { return bf ? launch_state_bf16(gp, s) : launch_state_f32(gp, s); });
         if (e != hipSuccess) return hip_fail(e, "gradient-state launch");
         ScanParams gc = cp;
         gc.partial = gp.partial; gc.part = state_part(gp); gc.U = w.GU; gc.n_sub = w.gsplit.n_sub;
@@ -567,7 +663,7 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         gc.s_bh_stride = (long long)w.gslots * g.d * g.Dp; gc.z_bh_stride = (long long)w.gslots * g.Dp;
         gc.t_first = 0; gc.mode = bidir ? kBidirGrad : kChunkRows;
         gc.suffix = bidir ? (float*)(ws + w.gsuffix_off) : nullptr;
-        if ((e = launch_scan(gc, s)) != hipSuccess) return hip_fail(e, "gradient scan launch");
+        if ((e = hip_step([&] { return launch_scan(gc, s); })) != hipSuccess) return hip_fail(e, "gradient scan launch");
         bp.st_hi = ws + w.thi_off; bp.st_lo = ws + w.tlo_off; bp.z = (const float*)(ws + w.z_off);
         bp.g_hi = ws + w.ghi_off; bp.g_lo = ws + w.glo_off;
         bp.gt_hi = ws + w.gthi_off; bp.gt_lo = ws + w.gtlo_off; bp.gz = (const float*)(ws + w.gz_off);
@@ -583,7 +679,7 @@ rehyat_status bwd_entry(const void* q, const void* k, const void* v, const void*
         lp.F = bp.F; lp.Tc = bp.Tc; lp.To = bp.To; lp.HW = bp.HW;
         bp.dq_lpt = choose_lpt_order(lp, bp.BH * bp.C * tpc, bn);
     }
-    e = bf ? launch_bwd_bf16(bp, s) : launch_bwd_f32(bp, s);
+    e = hip_step([&] { return bf ? launch_bwd_bf16(bp, s) : launch_bwd_f32(bp, s); });
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return REHYAT_OK;
 }
@@ -706,7 +802,7 @@ rehyat_status rehyat_step_state_init(rehyat_step_state* st, void* buf, size_t by
     st->B = B; st->H = H; st->tokens_per_frame = tokens_per_frame; st->head_dim = head_dim;
     st->chunk_frames = chunk_frames; st->overlap_frames = overlap_frames;
     st->feature_map = feature_map; st->dtype = dtype;
-    g_last_error.clear();
+    begin_call();
     return REHYAT_OK;
 }
 
@@ -739,13 +835,13 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes) ||
         overlaps(out, bytes, st->buf, st->bytes))
         return fail(REHYAT_EINVAL, "out must not overlap q, k, v or the state buffer");
-    g_last_error.clear();
+    begin_call();
     hipStream_t s = (hipStream_t)stream;
     char* base = (char*)st->buf;
     const int P = st->prev_frames * g.HW;
     const int cur = st->prev_slot;
     if (mlp) {  // phi of the chunk's queries and keys (the overlap frames' phi(k) is carried)
-        hipError_t e = launch_mlp(g, wq, wk, q, base + L.fq_off, n, 0, (int)n, k, base + L.fk_off, n, 0, (int)n, s);
+        hipError_t e = hip_step([&] { return launch_mlp(g, wq, wk, q, base + L.fq_off, n, 0, (int)n, k, base + L.fk_off, n, 0, (int)n, s); });
         if (e != hipSuccess) return hip_fail(e, "feature-map launch");
     }
 
@@ -771,7 +867,7 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
         lp.fq = base + L.fq_off;
         lp.fq_bh_stride = n * g.Dp;
     }
-    hipError_t e = g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s);
+    hipError_t e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s); });
     if (e != hipSuccess) return hip_fail(e, "local-attention launch");
 
     // 2. fold the rows leaving the window into (S, z)
@@ -798,7 +894,7 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
             sp.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; sp.fkp_bh_stride = (long long)g.To * g.HW * g.Dp;
         }
         sp.items_per_bh = state_items_per_bh(sp);
-        e = g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s);
+        e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s); });
         if (e != hipSuccess) return hip_fail(e, "block-state launch");
         ScanParams cp{};
         cp.partial = sp.partial; cp.part = state_part(sp);
@@ -810,7 +906,7 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
         cp.U = 1; cp.n_sub = sp.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
         cp.t_first = 1; cp.t_offset = 1; cp.f32_prep = g.dtype == REHYAT_F32;
         cp.mode = kCausal; cp.C = 1; cp.q = 0; cp.suffix = nullptr;
-        e = launch_scan(cp, s);
+        e = hip_step([&] { return launch_scan(cp, s); });
         if (e != hipSuccess) return hip_fail(e, "scan launch");
         nonempty = true;
     }
@@ -825,7 +921,7 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
             pc.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; pc.fk = base + L.fk_off; pc.fkd = base + L.fkp_off[cur ^ 1];
             pc.fprev_bh_stride = (long long)g.To * g.HW * g.Dp; pc.f_bh_stride = n * g.Dp; pc.f_cols = g.Dp;
         }
-        e = launch_prev_copy(pc, s);
+        e = hip_step([&] { return launch_prev_copy(pc, s); });
         if (e != hipSuccess) return hip_fail(e, "overlap copy launch");
     }
     st->prev_slot = keep_rows > 0 ? cur ^ 1 : cur;
@@ -890,7 +986,7 @@ rehyat_status rehyat_attn_fwd_lse(const void* q, const void* k, const void* v, v
             overlaps(out_f32, fb, out, bytes) || overlaps(out_f32, fb, lse, lbytes))
             return fail(REHYAT_EINVAL, "out_f32 must not overlap the other tensors");
     }
-    g_last_error.clear();
+    begin_call();
     return run_fwd(q, k, v, out, g, causal ? kCausal : kBidirectional, nullptr, nullptr, nullptr, nullptr,
                    nullptr, (hipStream_t)stream, nullptr, nullptr, lse, out_f32);
 }
@@ -913,10 +1009,19 @@ rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int
     if (!aligned16(x) || !aligned16(phi)) return fail(REHYAT_EINVAL, "tensor pointers must be 16-byte aligned");
     const size_t xb = (size_t)g.BH * rows * head_dim * g.elem, pb = 2 * xb;
     if (overlaps(x, xb, phi, pb)) return fail(REHYAT_EINVAL, "phi must not overlap x");
-    g_last_error.clear();
-    hipError_t e = launch_mlp(g, w, w, x, phi, rows, 0, rows, nullptr, nullptr, 0, 0, 0, (hipStream_t)stream);
+    begin_call();
+    hipError_t e = hip_step([&] { return launch_mlp(g, w, w, x, phi, rows, 0, rows, nullptr, nullptr, 0, 0, 0, (hipStream_t)stream); });
     return e == hipSuccess ? REHYAT_OK : hip_fail(e, "feature-map launch");
 }
+
+rehyat_status rehyat_workspace_release(void* stream) {
+    begin_call();
+    return arena_release((hipStream_t)stream);
+}
+
+void rehyat_debug_inject_hip_error(int step) { g_inject_at = step < 0 ? -1 : step; }
+
+int rehyat_debug_hip_steps(void) { return g_steps; }
 
 rehyat_status rehyat_set_profile_events(void* const* events, int n_events) {
     if (n_events == 0) {

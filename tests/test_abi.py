@@ -166,3 +166,80 @@ def test_key_block_partition(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, run.stdout + run.stderr
     assert " 0 violations" in run.stdout
+
+
+EHIP = 4
+
+
+def test_row_extent_limit():
+    """Rows of one (b, h) are addressed with 32-bit byte offsets: a clip whose
+    rows reach 2^31 bytes is rejected on the host; one row less passes the
+    checks (the armed fault-injection hook then stops the call at its first
+    HIP step, so nothing reaches the runtime)."""
+    lib = rh.load_library()
+    # bf16, head_dim 128: 256 bytes per row, limit 2^23 rows
+    assert _fwd(lib, F=8192, HW=1024, d=128) == EUNSUPPORTED
+    assert "2^31" in lib.rehyat_last_error().decode()
+    rh.debug_inject_hip_error(0)
+    try:
+        st = _fwd(lib, F=8191, HW=1024, d=128, out=FAKE * (1 << 16))
+    finally:
+        rh.debug_inject_hip_error(-1)
+    assert st == EHIP and "injected" in lib.rehyat_last_error().decode()
+    # fp32 at head_dim 64: 256 bytes per row as well
+    assert lib.rehyat_attn_fwd_f32(FAKE, FAKE, FAKE, FAKE * (1 << 16), 1, 1, 8192, 1024, 64, 3, 1, 1,
+                                   None) == EUNSUPPORTED
+    # the learned maps' feature rows are twice as wide: the limit halves
+    w = (ctypes.c_void_p * 4)()
+    mlp = rh._MlpC(FAKE, FAKE, FAKE, FAKE, 256)
+    st = lib.rehyat_attn_fwd_mlp(FAKE, FAKE, FAKE, FAKE * (1 << 16), 1, 1, 1, 4096, 1024, 128, 3, 1, 1,
+                                 ctypes.byref(mlp), ctypes.byref(mlp), None)
+    assert st == EUNSUPPORTED and "2^31" in lib.rehyat_last_error().decode()
+    # the streaming state checks the same bound on its chunk geometry
+    assert lib.rehyat_step_state_bytes(1, 1, 1 << 22, 128, 2, 1, 1, 1) == 0
+
+
+@pytest.mark.parametrize("entry", ["fwd", "fwd_none", "bidir", "partials", "bwd", "step"])
+def test_fault_injection_returns_ehip_before_any_hip_call(entry):
+    """A HIP failure forced from the host: with the hook armed at step 0 a
+    valid call stops at its first HIP step and reports REHYAT_EHIP with
+    the hook named; nothing is queued, so this runs without a GPU."""
+    lib = rh.load_library()
+    base = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, out=FAKE * 4, B=1, H=1, F=4, HW=8, d=64, Tc=1, To=1)
+    rh.debug_inject_hip_error(0)
+    try:
+        if entry == "fwd":
+            st = _fwd(lib, **base)
+        elif entry == "fwd_none":
+            st = _fwd(lib, **base, phi=0)
+        elif entry == "bidir":
+            st = lib.rehyat_attn_fwd_bidir(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, 1, 4, 8, 64, 1, 1, 1, None)
+        elif entry == "partials":
+            st = lib.rehyat_attn_fwd_partials(FAKE, FAKE * 2, FAKE * 3, 1, FAKE * 4, None, None, None, None,
+                                              1, 1, 4, 8, 64, 1, 1, 1, None)
+        elif entry == "bwd":
+            p = [FAKE * (i + 1) * 4096 for i in range(10)]
+            st = lib.rehyat_attn_bwd(p[0], p[1], p[2], p[3], None, p[4], p[5], p[6], p[7], p[8], 1,
+                                     1, 1, 4, 8, 64, 1, 1, 1, 1, None)
+        else:
+            s = rh._StepStateC()
+            need = lib.rehyat_step_state_bytes(1, 1, 8, 64, 1, 1, 1, 1)
+            assert lib.rehyat_step_state_init(ctypes.byref(s), FAKE * 4096, need, 1, 1, 8, 64, 1, 1, 1, 1) == 0
+            st = lib.rehyat_attn_step(ctypes.byref(s), FAKE, FAKE * 2, FAKE * 3, FAKE * 64, 1, None)
+            # a failed step leaves the stream where it was
+            assert s.frames_done == 0 and s.prev_frames == 0
+    finally:
+        rh.debug_inject_hip_error(-1)
+    msg = lib.rehyat_last_error().decode()
+    assert st == EHIP, (st, msg)
+    assert "injected failure at HIP step 0" in msg
+    assert rh.debug_hip_steps() == 1
+
+
+def test_fault_injection_hook_is_one_shot_and_disarms():
+    lib = rh.load_library()
+    rh.debug_inject_hip_error(0)
+    rh.debug_inject_hip_error(-1)
+    # disarmed: a call that fails validation reports that, not an injected failure
+    assert _fwd(lib, B=0) == EINVAL
+    assert "B and H" in lib.rehyat_last_error().decode()
