@@ -91,6 +91,26 @@ rehyat_status rehyat_attn_fwd(const void* q, const void* k, const void* v, void*
                               int chunk_frames, int overlap_frames, int feature_map,
                               void* stream);
 
+/*
+ * Allocation-free rehyat_attn_fwd, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, validation, kernels and results as
+ * rehyat_attn_fwd, but the workspace is a fixed file-scope device array of
+ * rehyat_noalloc_workspace_limit() bytes (64 MiB) on each device, held by the
+ * library until the process ends; no hipMalloc or hipFree is called.  A call
+ * that needs more workspace returns REHYAT_ENOMEM (a 21-frame clip of
+ * 1560-token frames with 12 heads of 128 needs about 20 MB with elu+1, about
+ * 40 MB with POLY2 or as a B = 2 pair).  Every call on a device shares the
+ * array: calls that overlap on one device (several streams or threads) race,
+ * so the caller must serialise them.
+ */
+rehyat_status rehyat_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                      int B, int H, int frames, int tokens_per_frame, int head_dim,
+                                      int chunk_frames, int overlap_frames, int feature_map,
+                                      void* stream);
+/* Bytes of the fixed workspace of rehyat_attn_fwd_noalloc. */
+size_t rehyat_noalloc_workspace_limit(void);
+
 /* Same contract with fp32 q, k, v, out. */
 rehyat_status rehyat_attn_fwd_f32(const void* q, const void* k, const void* v, void* out,
                                   int B, int H, int frames, int tokens_per_frame, int head_dim,

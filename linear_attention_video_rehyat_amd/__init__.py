@@ -17,7 +17,7 @@ import os
 
 __all__ = ["RehyatError", "attn_fwd", "attn_fwd_partials", "attn_fwd_lse", "attn_bwd", "StepState",
            "feature_map_id", "MlpWeights", "feature_mlp", "library_path", "load_library", "exported_symbols",
-           "workspace_release", "debug_inject_hip_error", "debug_hip_steps"]
+           "workspace_release", "debug_inject_hip_error", "debug_hip_steps", "attn_fwd_noalloc"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "librehyat.so")
@@ -28,7 +28,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every entry point declared in include/rehyat.h
 exported_symbols = (
-    "rehyat_attn_fwd", "rehyat_attn_fwd_f32", "rehyat_attn_fwd_partials",
+    "rehyat_attn_fwd", "rehyat_attn_fwd_noalloc", "rehyat_noalloc_workspace_limit",
+    "rehyat_attn_fwd_f32", "rehyat_attn_fwd_partials",
     "rehyat_attn_fwd_bidir", "rehyat_attn_fwd_bidir_f32", "rehyat_attn_fwd_bidir_partials",
     "rehyat_step_state_bytes", "rehyat_step_state_init", "rehyat_attn_step",
     "rehyat_feature_mlp", "rehyat_attn_fwd_mlp", "rehyat_attn_fwd_mlp_partials", "rehyat_attn_step_mlp",
@@ -75,7 +76,8 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, f_p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float)
     sig_fwd = [vp, vp, vp, vp] + [i] * 8 + [vp]
-    for name in ("rehyat_attn_fwd", "rehyat_attn_fwd_f32", "rehyat_attn_fwd_bidir", "rehyat_attn_fwd_bidir_f32"):
+    for name in ("rehyat_attn_fwd", "rehyat_attn_fwd_noalloc", "rehyat_attn_fwd_f32", "rehyat_attn_fwd_bidir",
+                 "rehyat_attn_fwd_bidir_f32"):
         fn = getattr(lib, name)
         fn.argtypes, fn.restype = sig_fwd, i
     for name in ("rehyat_attn_fwd_partials", "rehyat_attn_fwd_bidir_partials"):
@@ -100,6 +102,8 @@ def load_library():
     lib.rehyat_attn_fwd_lse.restype = i
     lib.rehyat_attn_bwd.argtypes = [vp] * 10 + [i] * 10 + [vp]
     lib.rehyat_attn_bwd.restype = i
+    lib.rehyat_noalloc_workspace_limit.argtypes = []
+    lib.rehyat_noalloc_workspace_limit.restype = ctypes.c_size_t
     lib.rehyat_workspace_release.argtypes = [vp]
     lib.rehyat_workspace_release.restype = i
     lib.rehyat_debug_inject_hip_error.argtypes = [i]
@@ -245,6 +249,29 @@ def attn_fwd(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, fe
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, frames,
               tokens_per_frame, d, chunk_frames, overlap_frames, feature_map_id(feature_map),
               _stream_handle(stream)))
+    return out
+
+
+def attn_fwd_noalloc(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, feature_map="elu1",
+                     out=None, stream=None):
+    """rehyat_attn_fwd_noalloc: the bf16 recurrent forward with its workspace in
+    the library's fixed per-device array (no device allocation by the library;
+    ``out`` should be passed by callers that allocate nothing either)."""
+    torch = _torch()
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if N != frames * tokens_per_frame:
+        raise RehyatError(1, f"N={N} != frames*tokens_per_frame={frames * tokens_per_frame}")
+    if q.dtype != torch.bfloat16:
+        raise RehyatError(2, "rehyat_attn_fwd_noalloc takes bf16 tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise RehyatError(1, "out must be a contiguous GPU tensor matching q")
+    _check(lib.rehyat_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, frames,
+                                       tokens_per_frame, d, chunk_frames, overlap_frames,
+                                       feature_map_id(feature_map), _stream_handle(stream)))
     return out
 
 

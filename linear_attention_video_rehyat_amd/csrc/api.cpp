@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "../../include/rehyat.h"
+#include "api_internal.h"
 #include "kernels.h"
 
 using namespace rehyat;
@@ -502,10 +503,13 @@ rehyat_status check_mlp(const rehyat_mlp_weights* wq, const rehyat_mlp_weights* 
     return REHYAT_OK;
 }
 
+// fixed_ws: the workspace is the device buffer it supplies, fixed_bytes bytes,
+// instead of the stream's arena (REHYAT_ENOMEM if the call needs more).
 rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, int B, int H,
                         int frames, int tpf, int d, int Tc, int To, int phi, int dtype, int mode,
                         void* stream, const rehyat_mlp_weights* wq = nullptr,
-                        const rehyat_mlp_weights* wk = nullptr) {
+                        const rehyat_mlp_weights* wk = nullptr, fixed_workspace_fn fixed_ws = nullptr,
+                        size_t fixed_bytes = 0) {
     Geometry g{};
     const bool mlp = phi == REHYAT_PHI_MLP2 && (wq || wk);
     rehyat_status st = check_common(g, B, H, frames, tpf, d, Tc, To, phi, dtype, mlp);
@@ -517,6 +521,25 @@ rehyat_status fwd_entry(const void* q, const void* k, const void* v, void* out, 
     const size_t bytes = (size_t)g.BH * g.N * g.d * g.elem;
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
         return fail(REHYAT_EINVAL, "out must not overlap q, k or v");
+    if (fixed_ws) {
+        const size_t need = fwd_workspace_bytes(g, mode);
+        if (need > fixed_bytes)
+            return fail(REHYAT_ENOMEM, "the call needs %zu bytes of workspace; the fixed scratch holds %zu",
+                        need, fixed_bytes);
+        begin_call();
+        char* ws = nullptr;
+        if (need) {  // the buffer's address: one HIP step (a runtime lookup)
+            rehyat_status wst = REHYAT_OK;
+            const hipError_t e = hip_step([&] {
+                wst = fixed_ws(&ws);
+                return wst == REHYAT_OK ? hipSuccess : hipErrorInvalidSymbol;
+            });
+            if (g_injected) return hip_fail(e, "fixed workspace lookup");
+            if (wst != REHYAT_OK) return wst;
+        }
+        return run_fwd_ws(q, k, v, out, g, mode, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream,
+                          wq, wk, nullptr, nullptr, ws);
+    }
     begin_call();
     return run_fwd(q, k, v, out, g, mode, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream, wq, wk);
 }
@@ -724,6 +747,21 @@ StepLayout step_layout(const Geometry& g) {
 }
 
 }  // namespace
+
+namespace rehyat {
+
+rehyat_status fwd_fixed_workspace(const void* q, const void* k, const void* v, void* out, int B, int H,
+                                  int frames, int tokens_per_frame, int head_dim, int chunk_frames,
+                                  int overlap_frames, int feature_map, void* stream, fixed_workspace_fn get_ws,
+                                  size_t ws_bytes) {
+    if (!get_ws) return fail(REHYAT_EINVAL, "internal: no fixed workspace");
+    return fwd_entry(q, k, v, out, B, H, frames, tokens_per_frame, head_dim, chunk_frames, overlap_frames,
+                     feature_map, REHYAT_BF16, kCausal, stream, nullptr, nullptr, get_ws, ws_bytes);
+}
+
+rehyat_status report_hip_error(int err, const char* what) { return hip_fail((hipError_t)err, what); }
+
+}  // namespace rehyat
 
 extern "C" {
 

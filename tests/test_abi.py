@@ -243,3 +243,26 @@ def test_fault_injection_hook_is_one_shot_and_disarms():
     # disarmed: a call that fails validation reports that, not an injected failure
     assert _fwd(lib, B=0) == EINVAL
     assert "B and H" in lib.rehyat_last_error().decode()
+
+
+def test_noalloc_validation_and_limit():
+    """The allocation-free forward validates like rehyat_attn_fwd and rejects
+    a call whose workspace exceeds its fixed array before any HIP call."""
+    lib = rh.load_library()
+    assert lib.rehyat_noalloc_workspace_limit() == 64 << 20
+    st = lib.rehyat_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE * 4, 0, 1, 4, 8, 64, 1, 1, 1, None)
+    assert st == EINVAL and "B and H" in lib.rehyat_last_error().decode()
+    # 105 frames of 1560 tokens, 12 heads of 128, elu+1: ~108 MB of workspace
+    big = 1 << 32
+    st = lib.rehyat_attn_fwd_noalloc(big, big * 2, big * 3, big * 4, 1, 12, 105, 1560, 128, 3, 1, 1, None)
+    assert st == 3 and "fixed scratch" in lib.rehyat_last_error().decode()
+    # valid calls, stopped at their first HIP step (the workspace lookup, or
+    # the launch when no chunk has a linear set and no workspace is needed)
+    for phi in (1, 0):
+        rh.debug_inject_hip_error(0)
+        try:
+            st = lib.rehyat_attn_fwd_noalloc(big, big * 2, big * 3, big * 4, 1, 12, 21, 1560, 128, 3, 1, phi, None)
+        finally:
+            rh.debug_inject_hip_error(-1)
+        assert st == EHIP and "injected" in lib.rehyat_last_error().decode()
+        assert rh.debug_hip_steps() == 1
