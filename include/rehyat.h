@@ -259,6 +259,46 @@ rehyat_status rehyat_attn_step_mlp(rehyat_step_state* st, const void* q, const v
                                    const rehyat_mlp_weights* phi_k, void* stream);
 
 /*
+ * Attention blocks (ReHyAt §3.1, first display equation: a DiT block is
+ * T_l(x) = f_l(A_l(x) + x); §4.3 "Model Hyperparameters": 15, 20 or 25 of the
+ * 30 blocks of Wan2.1 1.3B are converted to the hybrid attention).  The
+ * attention part with its projections, on x [B][N][C] token-major bf16,
+ * C = heads * head_dim, N = frames * tokens_per_frame:
+ *   q = x Wq^T + bq,  k = (x Wk^T + bk) / sqrt(head_dim),  v = x Wv^T + bv,
+ *   split into heads ([B][heads][N][head_dim], the attention layout);
+ *   A(x) = concat_heads(attn(q, k, v)) Wo^T + bo;   output x + A(x).
+ * attn is rehyat_attn_fwd with (chunk_frames, overlap_frames, feature_map) when
+ * the block is hybrid, and full bidirectional softmax attention (one chunk
+ * over the clip, no linear branch: the block before conversion) when not.
+ * f_l (the rest of the DiT block) is not part of this; q/k normalisation and
+ * rotary position embedding, which the pages do not describe, are not applied.
+ * The projections run on bf16 MFMA with fp32 accumulation; q, k, v and the
+ * attention output are bf16.  heads * head_dim must be a multiple of 128 and
+ * B*N*C*2 bytes below 2^31.  Workspace (q, k, v, the attention output, the
+ * attention's own workspace; two activation buffers for a stack) comes from
+ * the stream's arena.  feature_map: NONE, ELU1 or POLY2.
+ */
+typedef struct rehyat_block_weights {
+    const void* w_qkv;   /* [3C][C] bf16, out x in: rows 0..C-1 query, C..2C-1 key, 2C..3C-1 value */
+    const float* b_qkv;  /* [3C] fp32 */
+    const void* w_o;     /* [C][C] bf16, out x in */
+    const float* b_o;    /* [C] fp32 */
+} rehyat_block_weights;
+
+/* One block: out = x + A(x) (hybrid != 0: ReHyAt attention, 0: full softmax).
+ * out must not overlap x. */
+rehyat_status rehyat_block_fwd(const void* x, void* out, const rehyat_block_weights* w, int B, int frames,
+                               int tokens_per_frame, int heads, int head_dim, int hybrid, int chunk_frames,
+                               int overlap_frames, int feature_map, void* stream);
+
+/* A stack of n_blocks blocks, x_{l+1} = x_l + A_l(x_l) with weights w[l] and
+ * hybrid[l] selecting each block's attention (host arrays of n_blocks
+ * entries); out = x_{n_blocks}. */
+rehyat_status rehyat_stack_fwd(const void* x, void* out, const rehyat_block_weights* w, const int* hybrid,
+                               int n_blocks, int B, int frames, int tokens_per_frame, int heads, int head_dim,
+                               int chunk_frames, int overlap_frames, int feature_map, void* stream);
+
+/*
  * Training direction (ReHyAt §3.4: attention distillation and fine-tuning
  * backpropagate through the hybrid attention).  causal != 0 selects the
  * recurrent partition (rehyat_attn_fwd), causal == 0 the bidirectional one

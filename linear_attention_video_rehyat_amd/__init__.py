@@ -17,7 +17,8 @@ import os
 
 __all__ = ["RehyatError", "attn_fwd", "attn_fwd_partials", "attn_fwd_lse", "attn_bwd", "StepState",
            "feature_map_id", "MlpWeights", "feature_mlp", "library_path", "load_library", "exported_symbols",
-           "workspace_release", "debug_inject_hip_error", "debug_hip_steps", "attn_fwd_noalloc"]
+           "workspace_release", "debug_inject_hip_error", "debug_hip_steps", "attn_fwd_noalloc",
+           "BlockWeights", "block_fwd", "stack_fwd"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "librehyat.so")
@@ -33,7 +34,7 @@ exported_symbols = (
     "rehyat_attn_fwd_bidir", "rehyat_attn_fwd_bidir_f32", "rehyat_attn_fwd_bidir_partials",
     "rehyat_step_state_bytes", "rehyat_step_state_init", "rehyat_attn_step",
     "rehyat_feature_mlp", "rehyat_attn_fwd_mlp", "rehyat_attn_fwd_mlp_partials", "rehyat_attn_step_mlp",
-    "rehyat_attn_fwd_lse", "rehyat_attn_bwd",
+    "rehyat_attn_fwd_lse", "rehyat_attn_bwd", "rehyat_block_fwd", "rehyat_stack_fwd",
     "rehyat_workspace_release", "rehyat_debug_inject_hip_error", "rehyat_debug_hip_steps",
     "rehyat_set_profile_events", "rehyat_status_string", "rehyat_last_error", "rehyat_version",
 )
@@ -54,6 +55,11 @@ class _StepStateC(ctypes.Structure):
         ("prev_frames", ctypes.c_int), ("prev_slot", ctypes.c_int), ("state_nonempty", ctypes.c_int),
         ("frames_done", ctypes.c_longlong),
     ]
+
+
+class _BlockWeightsC(ctypes.Structure):
+    _fields_ = [("w_qkv", ctypes.c_void_p), ("b_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
+                ("b_o", ctypes.c_void_p)]
 
 
 class _MlpC(ctypes.Structure):
@@ -100,6 +106,11 @@ def load_library():
     lib.rehyat_attn_step_mlp.restype = i
     lib.rehyat_attn_fwd_lse.argtypes = [vp] * 6 + [i] * 10 + [vp]
     lib.rehyat_attn_fwd_lse.restype = i
+    bw = ctypes.POINTER(_BlockWeightsC)
+    lib.rehyat_block_fwd.argtypes = [vp, vp, bw] + [i] * 9 + [vp]
+    lib.rehyat_block_fwd.restype = i
+    lib.rehyat_stack_fwd.argtypes = [vp, vp, bw, ctypes.POINTER(ctypes.c_int)] + [i] * 9 + [vp]
+    lib.rehyat_stack_fwd.restype = i
     lib.rehyat_attn_bwd.argtypes = [vp] * 10 + [i] * 10 + [vp]
     lib.rehyat_attn_bwd.restype = i
     lib.rehyat_noalloc_workspace_limit.argtypes = []
@@ -372,6 +383,76 @@ def debug_inject_hip_error(step: int):
 def debug_hip_steps() -> int:
     """HIP steps (runtime calls and launches) of the last call on this thread."""
     return int(load_library().rehyat_debug_hip_steps())
+
+
+class BlockWeights:
+    """Projection weights of one attention block (include/rehyat.h,
+    rehyat_block_weights): w_qkv [3C, C] and w_o [C, C] bf16 (out x in), b_qkv
+    [3C] and b_o [C] float32, contiguous on the GPU."""
+
+    def __init__(self, w_qkv, b_qkv, w_o, b_o):
+        torch = _torch()
+        for name, t in (("w_qkv", w_qkv), ("b_qkv", b_qkv), ("w_o", w_o), ("b_o", b_o)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise RehyatError(1, f"{name} must be a contiguous GPU tensor")
+        if w_qkv.dtype != torch.bfloat16 or w_o.dtype != torch.bfloat16:
+            raise RehyatError(1, "w_qkv and w_o must be bfloat16")
+        if b_qkv.dtype != torch.float32 or b_o.dtype != torch.float32:
+            raise RehyatError(1, "b_qkv and b_o must be float32")
+        C = w_o.shape[0]
+        if (w_qkv.shape != (3 * C, C) or w_o.shape != (C, C) or tuple(b_qkv.shape) != (3 * C,)
+                or tuple(b_o.shape) != (C,)):
+            raise RehyatError(1, "expected w_qkv [3C, C], b_qkv [3C], w_o [C, C], b_o [C]")
+        self.tensors = (w_qkv, b_qkv, w_o, b_o)
+        self.C = C
+        self._c = _BlockWeightsC(w_qkv.data_ptr(), b_qkv.data_ptr(), w_o.data_ptr(), b_o.data_ptr())
+
+
+def _check_block_x(x, weights):
+    torch = _torch()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 3 or x.dtype != torch.bfloat16:
+        raise RehyatError(1, "x must be a contiguous bfloat16 [B, N, C] GPU tensor")
+    if x.shape[2] != weights.C:
+        raise RehyatError(1, f"x has {x.shape[2]} channels, the weights {weights.C}")
+
+
+def block_fwd(x, weights, frames, tokens_per_frame, heads, hybrid=True, chunk_frames=3, overlap_frames=1,
+              feature_map="elu1", out=None, stream=None):
+    """One attention block, out = x + A(x) (rehyat_block_fwd): x [B, N, C] bf16,
+    N = frames * tokens_per_frame, C = heads * head_dim; hybrid=False gives the
+    block with full softmax attention."""
+    torch = _torch()
+    lib = load_library()
+    _check_block_x(x, weights)
+    B, N, C = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.rehyat_block_fwd(x.data_ptr(), out.data_ptr(), ctypes.byref(weights._c), B, frames, tokens_per_frame,
+                                heads, C // heads, 1 if hybrid else 0, chunk_frames, overlap_frames,
+                                feature_map_id(feature_map), _stream_handle(stream)))
+    return out
+
+
+def stack_fwd(x, weights, hybrid, frames, tokens_per_frame, heads, chunk_frames=3, overlap_frames=1,
+              feature_map="elu1", out=None, stream=None):
+    """A stack of blocks (rehyat_stack_fwd): weights is a list of BlockWeights,
+    hybrid a list of booleans of the same length (which blocks use the hybrid
+    attention)."""
+    torch = _torch()
+    lib = load_library()
+    if len(weights) != len(hybrid) or not weights:
+        raise RehyatError(1, "weights and hybrid must be non-empty lists of the same length")
+    for w in weights:
+        _check_block_x(x, w)
+    B, N, C = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    arr = (_BlockWeightsC * len(weights))(*[w._c for w in weights])
+    flags = (ctypes.c_int * len(hybrid))(*[1 if h else 0 for h in hybrid])
+    _check(lib.rehyat_stack_fwd(x.data_ptr(), out.data_ptr(), arr, flags, len(weights), B, frames,
+                                tokens_per_frame, heads, C // heads, chunk_frames, overlap_frames,
+                                feature_map_id(feature_map), _stream_handle(stream)))
+    return out
 
 
 def set_profile_events(events):

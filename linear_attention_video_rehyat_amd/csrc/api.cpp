@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <map>
 #include <memory>
 #include <cstdarg>
@@ -746,6 +747,122 @@ StepLayout step_layout(const Geometry& g) {
     return L;
 }
 
+// ---------------------------------------------------------------- attention blocks
+// The attention part of a DiT block, T_l(x) = f_l(A_l(x) + x) (ReHyAt §3.1,
+// first display equation): x [B][N][C] token-major bf16, C = H d;
+// A(x) = concat_heads(attn(x Wq^T + bq, (x Wk^T + bk)/sqrt(d), x Wv^T + bv)) Wo^T + bo.
+// attn is the hybrid attention (hybrid != 0, the given chunk geometry and
+// feature map) or full bidirectional softmax attention (hybrid == 0: one chunk
+// over the clip, no linear branch -- the block as it was before conversion).
+struct BlockGeometry {
+    Geometry attn;  // the attention call's geometry (dense: T_c = F, T_o = 0, no phi)
+    int mode;
+    long long T;    // tokens B N
+    int C;
+    size_t act_bytes, q_off, k_off, v_off, y_off, attn_off, attn_bytes;
+};
+
+rehyat_status check_block(BlockGeometry& bg, int B, int frames, int tpf, int heads, int d, int hybrid, int Tc, int To,
+                          int phi) {
+    Geometry g{};
+    rehyat_status st = hybrid ? check_common(g, B, heads, frames, tpf, d, Tc, To, phi, REHYAT_BF16)
+                              : check_common(g, B, heads, frames, tpf, d, frames, 0, REHYAT_PHI_NONE, REHYAT_BF16);
+    if (st != REHYAT_OK) return st;
+    const int C = heads * d;
+    if (!proj_shape_ok(C, 3 * C, d) || !proj_shape_ok(C, C, d))
+        return fail(REHYAT_EUNSUPPORTED, "block width heads*head_dim = %d must be a multiple of 128", C);
+    const long long T = (long long)B * g.N;
+    if (T * C * 2 >= (1LL << 31))
+        return fail(REHYAT_EUNSUPPORTED, "block activations of %lld bytes exceed the 2^31-byte extent the projections "
+                    "address", T * C * 2);
+    bg.attn = g;
+    bg.mode = kCausal;
+    bg.T = T;
+    bg.C = C;
+    bg.act_bytes = (size_t)T * C * 2;
+    const size_t a = align256(bg.act_bytes);
+    bg.q_off = 0;
+    bg.k_off = a;
+    bg.v_off = 2 * a;
+    bg.y_off = 3 * a;
+    bg.attn_off = 4 * a;
+    bg.attn_bytes = fwd_workspace_bytes(g, kCausal);
+    return REHYAT_OK;
+}
+
+rehyat_status check_block_weights(const rehyat_block_weights* w) {
+    if (!w) return fail(REHYAT_EINVAL, "null block weights");
+    if (!w->w_qkv || !w->b_qkv || !w->w_o || !w->b_o) return fail(REHYAT_EINVAL, "null block weight pointer");
+    if (!aligned16(w->w_qkv) || !aligned16(w->b_qkv) || !aligned16(w->w_o) || !aligned16(w->b_o))
+        return fail(REHYAT_EINVAL, "block weights must be 16-byte aligned");
+    return REHYAT_OK;
+}
+
+// One block's launches: x -> out through q, k, v, y in the workspace `ws`.
+rehyat_status run_block(const void* x, void* out, const rehyat_block_weights& w, const BlockGeometry& bg, char* ws,
+                        hipStream_t s) {
+    const Geometry& g = bg.attn;
+    ProjParams pq{};
+    pq.mode = kProjQKV;
+    pq.x = x; pq.w = w.w_qkv; pq.bias = w.b_qkv;
+    pq.q = ws + bg.q_off; pq.k = ws + bg.k_off; pq.v = ws + bg.v_off;
+    pq.k_scale = 1.0f / std::sqrt((float)g.d);
+    pq.T = (int)bg.T; pq.N = (int)g.N; pq.H = g.H; pq.d = g.d; pq.c_in = bg.C; pq.n_out = 3 * bg.C;
+    hipError_t e = hip_step([&] { return launch_proj_bf16(pq, s); });
+    if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
+    rehyat_status st = run_fwd_ws(ws + bg.q_off, ws + bg.k_off, ws + bg.v_off, ws + bg.y_off, g, bg.mode, nullptr,
+                                  nullptr, nullptr, nullptr, nullptr, s, nullptr, nullptr, nullptr, nullptr,
+                                  bg.attn_bytes ? ws + bg.attn_off : nullptr);
+    if (st != REHYAT_OK) return st;
+    ProjParams po{};
+    po.mode = kProjOut;
+    po.x = ws + bg.y_off; po.x_bytes = (int)bg.act_bytes; po.w = w.w_o; po.bias = w.b_o;
+    po.resid = x; po.out = out;
+    po.T = (int)bg.T; po.N = (int)g.N; po.H = g.H; po.d = g.d; po.c_in = bg.C; po.n_out = bg.C;
+    e = hip_step([&] { return launch_proj_bf16(po, s); });
+    if (e != hipSuccess) return hip_fail(e, "output projection launch");
+    return REHYAT_OK;
+}
+
+// A stack of n blocks, x_{l+1} = x_l + A_l(x_l) (f_l taken as the identity:
+// the rest of the DiT block is not part of the attention).  Activations
+// alternate between two workspace buffers; the last block writes `out`.
+rehyat_status stack_entry(const void* x, void* out, const rehyat_block_weights* w, const int* hybrid, int n_blocks,
+                          int B, int frames, int tpf, int heads, int d, int Tc, int To, int phi, void* stream) {
+    if (n_blocks < 1) return fail(REHYAT_EINVAL, "n_blocks must be >= 1 (got %d)", n_blocks);
+    if (!w || !hybrid) return fail(REHYAT_EINVAL, "null weights or hybrid flags");
+    if (phi == REHYAT_PHI_MLP2) return fail(REHYAT_EUNSUPPORTED, "the blocks take NONE, ELU1 or POLY2 feature maps");
+    BlockGeometry bh{}, bd{};
+    bool any_h = false, any_d = false;
+    for (int l = 0; l < n_blocks; ++l) (hybrid[l] ? any_h : any_d) = true;
+    rehyat_status st;
+    if (any_h && (st = check_block(bh, B, frames, tpf, heads, d, 1, Tc, To, phi)) != REHYAT_OK) return st;
+    if ((any_d || !any_h) && (st = check_block(bd, B, frames, tpf, heads, d, 0, Tc, To, phi)) != REHYAT_OK) return st;
+    for (int l = 0; l < n_blocks; ++l)
+        if ((st = check_block_weights(&w[l])) != REHYAT_OK) return st;
+    if (!x || !out) return fail(REHYAT_EINVAL, "null tensor pointer");
+    if (!aligned16(x) || !aligned16(out)) return fail(REHYAT_EINVAL, "tensor pointers must be 16-byte aligned");
+    const BlockGeometry& b0 = any_h ? bh : bd;
+    if (overlaps(x, b0.act_bytes, out, b0.act_bytes)) return fail(REHYAT_EINVAL, "out must not overlap x");
+    begin_call();
+    hipStream_t s = (hipStream_t)stream;
+    const size_t a = align256(b0.act_bytes);
+    const size_t attn = std::max(any_h ? bh.attn_bytes : 0, any_d ? bd.attn_bytes : 0);
+    const size_t per_block = 4 * a + align256(attn);
+    const size_t total = per_block + (n_blocks > 1 ? 2 * a : 0);
+    ArenaLease lease;
+    if ((st = arena_acquire(total, s, lease)) != REHYAT_OK) return st;
+    char* ws = lease.ptr;
+    const void* cur = x;
+    for (int l = 0; l < n_blocks; ++l) {
+        void* dst = l == n_blocks - 1 ? out : ws + per_block + (size_t)(l & 1) * a;
+        st = run_block(cur, dst, w[l], hybrid[l] ? bh : bd, ws, s);
+        if (st != REHYAT_OK) return st;
+        cur = dst;
+    }
+    return REHYAT_OK;
+}
+
 }  // namespace
 
 namespace rehyat {
@@ -1035,6 +1152,21 @@ rehyat_status rehyat_attn_bwd(const void* q, const void* k, const void* v, const
                               int overlap_frames, int feature_map, int causal, void* stream) {
     return bwd_entry(q, k, v, out, out_f32, lse, dout, dq, dk, dv, dtype, B, H, frames, tokens_per_frame, head_dim,
                      chunk_frames, overlap_frames, feature_map, causal ? kCausal : kBidirectional, stream);
+}
+
+rehyat_status rehyat_block_fwd(const void* x, void* out, const rehyat_block_weights* w, int B, int frames,
+                               int tokens_per_frame, int heads, int head_dim, int hybrid, int chunk_frames,
+                               int overlap_frames, int feature_map, void* stream) {
+    const int flag = hybrid ? 1 : 0;
+    return stack_entry(x, out, w, &flag, 1, B, frames, tokens_per_frame, heads, head_dim, chunk_frames,
+                       overlap_frames, feature_map, stream);
+}
+
+rehyat_status rehyat_stack_fwd(const void* x, void* out, const rehyat_block_weights* w, const int* hybrid,
+                               int n_blocks, int B, int frames, int tokens_per_frame, int heads, int head_dim,
+                               int chunk_frames, int overlap_frames, int feature_map, void* stream) {
+    return stack_entry(x, out, w, hybrid, n_blocks, B, frames, tokens_per_frame, heads, head_dim, chunk_frames,
+                       overlap_frames, feature_map, stream);
 }
 
 rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int H, int rows, int head_dim,

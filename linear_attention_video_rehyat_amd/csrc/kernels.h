@@ -285,6 +285,26 @@ struct MlpParams {
     int grid;                         // workgroups (bf16 kernel: at most one per CU)
 };
 
+// Projections of the attention block (bf16 MFMA GEMM, C^T = W X^T per tile):
+//  kProjQKV: x [T][C] token-major, w [3C][C] (out x in), bias [3C] ->
+//            q, k, v [B][H][N][d] (k times k_scale)
+//  kProjOut: x = the attention output [B][H][N][d], w [C][C], bias [C], resid
+//            [T][C] -> out [T][C] = resid + x Wo^T + bias
+enum ProjMode { kProjQKV = 0, kProjOut = 1 };
+struct ProjParams {
+    int mode;
+    const void* x;                    // bf16, see above
+    int x_bytes;                      // kProjOut: bytes of the attention output (reads past it give 0)
+    const void* w;                    // bf16 [n_out][c_in]
+    const float* bias;                // [n_out]
+    void* q; void* k; void* v;        // kProjQKV outputs
+    float k_scale;
+    const void* resid; void* out;     // kProjOut
+    int T, N, H, d, c_in, n_out;      // tokens (B*N), tokens per batch entry, heads, head_dim
+};
+bool proj_shape_ok(int c_in, int n_out, int head_dim);
+hipError_t launch_proj_bf16(const ProjParams& p, hipStream_t s);
+
 hipError_t launch_local_bf16(const LocalParams& p, hipStream_t s);
 hipError_t launch_local_f32(const LocalParams& p, hipStream_t s);
 hipError_t launch_state_bf16(const StateParams& p, hipStream_t s);

@@ -133,3 +133,31 @@ def make_mlp_weights(seed_id: int, side: int, H: int, head_dim: int, hidden: int
     w1t = torch.from_numpy(w1).to(tdt).to(torch.float32)
     w2t = torch.from_numpy(w2).to(tdt).to(torch.float32)
     return w1t, torch.from_numpy(b1), w2t, torch.from_numpy(b2)
+
+
+def make_block_input(seed_id: int, B: int, N: int, C: int, device="cpu"):
+    """Seeded block input x ~ N(0, 1), [B, N, C] bf16 (seed default_rng(1000*seed_id + 6))."""
+    x = _draw(1000 * seed_id + 6, (B, N, C))
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t.to(device) if device != "cpu" else t
+
+
+def make_block_weights(seed_id: int, layer: int, C: int, out_gain: float = 1.0):
+    """Seeded synthetic projection weights of one attention block (there are no
+    trained weights to load): w_qkv [3C, C] ~ N(0, 1/C) (so q, k, v of a unit-rms
+    input are unit-rms), b_qkv [3C] ~ N(0, 0.1^2), w_o [C, C] ~ N(0, out_gain^2/C),
+    b_o [C] ~ N(0, 0.1^2); the weights rounded to bf16 (returned as bf16), the
+    biases float32.  Seeds default_rng(1000*seed_id + 100 + 4*layer + i)."""
+    base = 1000 * seed_id + 100 + 4 * layer
+    w_qkv = _draw(base + 0, (3 * C, C), 1.0 / math.sqrt(C))
+    b_qkv = _draw(base + 1, (3 * C,), 0.1)
+    w_o = _draw(base + 2, (C, C), out_gain / math.sqrt(C))
+    b_o = _draw(base + 3, (C,), 0.1)
+    return (torch.from_numpy(w_qkv).to(torch.bfloat16), torch.from_numpy(b_qkv),
+            torch.from_numpy(w_o).to(torch.bfloat16), torch.from_numpy(b_o))
+
+
+def converted_blocks(n_converted: int, n_blocks: int = 30):
+    """Which of the n_blocks blocks use the hybrid attention: the first
+    n_converted (the pages name how many blocks are converted, not which)."""
+    return [i < n_converted for i in range(n_blocks)]

@@ -412,3 +412,54 @@ def grad_q_rows(q, k, v, dy, frames, tokens_per_frame, chunk_frames, overlap_fra
                         dq = dq + 2.0 * qi * dphi[d:]
                 out[b, h, r] = dq
     return out
+
+
+# ---------------------------------------------------------------------------
+# attention blocks (ReHyAt §3.1, first display equation: T_l(x) = f_l(A_l(x) + x))
+# ---------------------------------------------------------------------------
+
+def block_attention(x, w_qkv, b_qkv, w_o, b_o, heads, frames, tokens_per_frame, hybrid=True, chunk_frames=3,
+                    overlap_frames=1, phi="elu1", rows=None):
+    """fp64 A(x) of one attention block, x [B, N, C] (C = heads d):
+    q = x Wq^T + bq, k = (x Wk^T + bk)/sqrt(d), v = x Wv^T + bv (w_qkv rows: q, k,
+    v), split into heads; y = the hybrid attention of the definition form
+    (hybrid) or full softmax attention (one chunk over the clip, no linear
+    set); A(x) = concat_heads(y) Wo^T + bo.  ``rows``: output token rows
+    (every row of q, k, v is formed).  Returns [B, R, C]."""
+    x = _f64(x)
+    w_qkv, b_qkv, w_o, b_o = (_f64(a) for a in (w_qkv, b_qkv, w_o, b_o))
+    B, N, C = x.shape
+    d = C // heads
+    assert heads * d == C and w_qkv.shape == (3 * C, C) and w_o.shape == (C, C)
+    qkv = x @ w_qkv.T + b_qkv                                     # [B, N, 3C]
+
+    def split(a):                                                 # [B, N, C] -> [B, H, N, d]
+        return np.ascontiguousarray(a.reshape(B, N, heads, d).transpose(0, 2, 1, 3))
+
+    q, k, v = split(qkv[..., :C]), split(qkv[..., C:2 * C]) / np.sqrt(d), split(qkv[..., 2 * C:])
+    if hybrid:
+        y = definition(q, k, v, frames, tokens_per_frame, chunk_frames, overlap_frames, phi, rows=rows)
+    else:
+        y = definition(q, k, v, frames, tokens_per_frame, frames, 0, "none", rows=rows)
+    R = y.shape[2]
+    y = y.transpose(0, 2, 1, 3).reshape(B, R, C)                  # concat heads
+    return y @ w_o.T + b_o
+
+
+def block_forward(x, w_qkv, b_qkv, w_o, b_o, heads, frames, tokens_per_frame, hybrid=True, chunk_frames=3,
+                  overlap_frames=1, phi="elu1", rows=None):
+    """fp64 x + A(x) (at ``rows`` if given)."""
+    x = _f64(x)
+    a = block_attention(x, w_qkv, b_qkv, w_o, b_o, heads, frames, tokens_per_frame, hybrid, chunk_frames,
+                        overlap_frames, phi, rows)
+    return (x if rows is None else x[:, np.asarray(rows)]) + a
+
+
+def stack_forward(x, weights, hybrid, heads, frames, tokens_per_frame, chunk_frames=3, overlap_frames=1,
+                  phi="elu1"):
+    """fp64 stack x_{l+1} = x_l + A_l(x_l) over the blocks (f_l taken as the
+    identity); weights: list of (w_qkv, b_qkv, w_o, b_o), hybrid: list of bools."""
+    x = _f64(x)
+    for w, hy in zip(weights, hybrid):
+        x = block_forward(x, *w, heads, frames, tokens_per_frame, hy, chunk_frames, overlap_frames, phi)
+    return x

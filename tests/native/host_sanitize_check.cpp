@@ -28,6 +28,10 @@ hipError_t launch_bwd_dsum(const BwdParams&, float*, bool, hipStream_t) { ++g_la
 hipError_t launch_bwd_bf16(const BwdParams&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_bwd_f32(const BwdParams&, hipStream_t) { ++g_launches; return hipSuccess; }
 void dq_launch_shape(const BwdParams&, int& tiles_per_chunk, int& key_tile) { tiles_per_chunk = 1; key_tile = 64; }
+hipError_t launch_proj_bf16(const ProjParams&, hipStream_t) { ++g_launches; return hipSuccess; }
+bool proj_shape_ok(int c_in, int n_out, int head_dim) {
+    return c_in % 32 == 0 && n_out % 128 == 0 && head_dim % 32 == 0 && c_in % head_dim == 0;
+}
 bool phi_mlp_hidden_ok(int hidden) { return hidden == 32 || hidden == 64 || hidden == 128 || hidden == 256; }
 int local_bf16_tile_rows(int) { return 256; }
 int local_bf16_key_tile(int) { return 128; }
@@ -117,10 +121,24 @@ int main() {
     st.prev_frames = 0;
     expect(rehyat_attn_step_mlp(&st, P(1), P(2), P(3), P(4), 1, &w, &w, nullptr), I, "step mlp on elu1 state");
     expect(rehyat_set_profile_events(nullptr, 3), I, "profile events");
+    // ---- attention blocks
+    rehyat_block_weights bw{P(30), (const float*)P(31), P(32), (const float*)P(33)};
+    rehyat_block_weights bwn = bw;
+    bwn.b_o = nullptr;
+    const int hyb[3] = {1, 0, 1};
+    expect(rehyat_block_fwd(P(1), P(2), nullptr, 1, 4, 8, 2, 64, 1, 1, 1, 1, nullptr), I, "block null weights");
+    expect(rehyat_block_fwd(P(1), P(2), &bwn, 1, 4, 8, 2, 64, 1, 1, 1, 1, nullptr), I, "block null b_o");
+    expect(rehyat_block_fwd(P(1), P(2), &bw, 1, 4, 8, 3, 32, 1, 1, 1, 1, nullptr), U, "block width 96");
+    expect(rehyat_block_fwd(P(1), (char*)P(1) + 64, &bw, 1, 4, 8, 2, 64, 1, 1, 1, 1, nullptr), I, "block overlap");
+    expect(rehyat_block_fwd(P(1), P(2), &bw, 1, 4, 8, 2, 64, 1, 1, 1, 3, nullptr), U, "block mlp");
+    expect(rehyat_stack_fwd(P(1), P(2), &bw, hyb, 0, 1, 4, 8, 2, 64, 1, 1, 1, nullptr), I, "stack n=0");
+    expect(rehyat_stack_fwd(P(1), P(2), &bw, nullptr, 1, 1, 4, 8, 2, 64, 1, 1, 1, nullptr), I, "stack null flags");
+    expect(rehyat_block_fwd(P(1), P(2), &bw, 1, 1 << 13, 1 << 10, 2, 64, 1, 3, 1, 1, nullptr), U, "block extent");
     // ---- valid calls stopped at their first HIP step by the armed hook
     struct { const char* name; int want; } armed[] = {{"fwd", H}, {"fwd none", H}, {"bidir f32", H}, {"partials", H},
                                                       {"lse", H}, {"bwd", H}, {"step", H}, {"mlp", H},
-                                                      {"feature mlp", H}, {"release", H}};
+                                                      {"feature mlp", H}, {"release", H}, {"block", H},
+                                                      {"stack", H}};
     for (int i = 0; i < (int)(sizeof armed / sizeof armed[0]); ++i) {
         rehyat_debug_inject_hip_error(0);
         int s = -1;
@@ -140,6 +158,12 @@ int main() {
         case 7: s = rehyat_attn_fwd_mlp(P(1), P(2), P(3), P(4), 1, 1, 2, 7, 33, 64, 3, 1, 1, &w, &w, nullptr); break;
         case 8: s = rehyat_feature_mlp(P(1), P(2), 1, 1, 2, 33, 64, &w, nullptr); break;
         case 9: s = rehyat_workspace_release(nullptr); break;
+        case 10: s = rehyat_block_fwd(P(1), P(2), &bw, 1, 5, 40, 2, 64, 1, 2, 1, 1, nullptr); break;
+        case 11: {
+            rehyat_block_weights three[3] = {bw, bw, bw};
+            s = rehyat_stack_fwd(P(1), P(3), three, hyb, 3, 1, 5, 40, 2, 64, 2, 1, 2, nullptr);
+            break;
+        }
         }
         expect(s, armed[i].want, armed[i].name);
         if (!std::strstr(rehyat_last_error(), "injected")) {
