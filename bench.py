@@ -318,8 +318,76 @@ def learned_map_bench(rh, hip, inputs, q, k, v, out, w, Tc, To, hidden, steps, c
                                "hbm_gbs": round(rows * d * 2 * 3 / (mlp_ms / 1000.0) / 1e9, 1)}}
 
 
-def cpu_baseline(w, q, k, v, Tc, To, phi, target_s=15.0):
-    """fp64 oracle (definition form) on a bounded, chunk-stratified sample of query rows."""
+def block_bench(rh, inputs, w, Tc, To, phi, steps, attn_ms, dense_attn_ms):
+    """The attention blocks around the hybrid attention at the Wan2.1-1.3B
+    shape (C = 12 x 128 = 1536, seeded synthetic projection weights): one block
+    with the hybrid attention and one with full softmax attention (the block
+    before conversion), and stacks of 30 blocks with 25, 20, 15 and 0 of them
+    converted (the pages' configurations; the first n converted).  The
+    projections' share of a block is its time minus the attention's; their
+    algorithmic work is 8 T C^2 FLOP per block (QKV 6 T C^2, output 2 T C^2)."""
+    import torch
+    H, d = w.H, w.head_dim
+    C = H * d
+    T = w.B * w.N
+    x = inputs.make_block_input(w.seed_id, w.B, w.N, C, device="cuda")
+    wts = [rh.BlockWeights(*(t.cuda() for t in inputs.make_block_weights(w.seed_id, l, C))) for l in range(30)]
+    out = torch.empty_like(x)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    hyb_ms = timed(lambda: rh.block_fwd(x, wts[0], w.frames, w.tokens_per_frame, H, True, Tc, To, phi, out=out),
+                   steps)
+    den_ms = timed(lambda: rh.block_fwd(x, wts[0], w.frames, w.tokens_per_frame, H, False, Tc, To, phi, out=out),
+                   max(2, steps // 4))
+    proj_flops = 8.0 * T * C * C
+    proj_ms = hyb_ms - attn_ms
+    res = {"C": C, "block_hybrid_ms": round(hyb_ms, 4), "block_dense_ms": round(den_ms, 4),
+           "projections_ms": round(proj_ms, 4), "projection_flops": proj_flops,
+           "projections_tflops": round(proj_flops / (proj_ms / 1000.0) / 1e12, 1),
+           "projections_frac": round(proj_flops / (proj_ms / 1000.0) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "dense_block_projections_ms": round(den_ms - dense_attn_ms, 4) if dense_attn_ms else None}
+    stacks = {}
+    for n_conv in (25, 20, 15, 0):
+        flags = inputs.converted_blocks(n_conv, 30)
+        ms = timed(lambda: rh.stack_fwd(x, wts, flags, w.frames, w.tokens_per_frame, H, Tc, To, phi, out=out), 2)
+        stacks[f"converted_{n_conv}_of_30"] = {"ms": round(ms, 3), "tokens_per_s": round(T / (ms / 1000.0), 1)}
+    res["stack_30_blocks"] = stacks
+    res["stack_speedup_25_of_30"] = round(stacks["converted_0_of_30"]["ms"] / stacks["converted_25_of_30"]["ms"], 3)
+    return res
+
+
+def cpu_info():
+    """Host CPU model and logical CPU counts (the machine and what this process may use)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "logical_cpus": os.cpu_count()}
+
+
+def cpu_baseline(w, q, k, v, Tc, To, phi, target_s=15.0, full_limit_s=60.0):
+    """fp64 oracle (definition form) on the host cores: every output row when a
+    512-row calibration puts the full output within full_limit_s, else a
+    random row sample sized to about target_s."""
     import numpy as np
     from oracle import oracle as O
     q64, k64, v64 = (x.double().numpy() for x in (q, k, v))
@@ -329,21 +397,24 @@ def cpu_baseline(w, q, k, v, Tc, To, phi, target_s=15.0):
     def rows_for(n):
         return np.sort(rng.choice(N, size=n, replace=False)).astype(np.int64)
 
-    # calibrate the rate on a sample large enough that start-up costs do not
-    # dominate, then size the timed sample for about target_s seconds
     n = 512
     t0 = time.perf_counter()
     O.definition(q64, k64, v64, w.frames, w.tokens_per_frame, Tc, To, phi, rows=rows_for(n))
     dt = time.perf_counter() - t0
-    n2 = int(max(32, min(N, n * target_s / max(dt, 1e-3))))
-    rows = rows_for(n2)
+    full = dt * N / n <= full_limit_s
+    n2 = N if full else int(max(32, min(N, n * target_s / max(dt, 1e-3))))
+    rows = None if full else rows_for(n2)
     t0 = time.perf_counter()
     O.definition(q64, k64, v64, w.frames, w.tokens_per_frame, Tc, To, phi, rows=rows)
     dt = time.perf_counter() - t0
     tokens = w.B * n2
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": O.max_threads(), "kind": "oracle",
-            "sample": f"{n2} random query rows of {N} per (b,h), all {w.B * w.H} heads, fp64 "
-                      f"definition form, {dt:.1f} s"}
+    what = (f"every output row ({N} per (b,h)), all {w.B * w.H} heads" if full else
+            f"{n2} random query rows of {N} per (b,h), all {w.B * w.H} heads")
+    res = {"value": tokens / dt, "unit": "tokens/s", "cores": O.max_threads(), "kind": "oracle",
+           "sample": f"{what}, fp64 definition form, {dt:.1f} s", "seconds": round(dt, 2),
+           "full_output": full}
+    res.update(cpu_info())
+    return res
 
 
 def main():
@@ -361,6 +432,7 @@ def main():
     ap.add_argument("--no-length", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-blocks", action="store_true")
     ap.add_argument("--learned-hidden", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -467,6 +539,13 @@ def main():
     if not args.no_length and w.name == "wan_21x30x52" and Tc == 3 and phi == "elu1":
         length = length_scaling_bench(rh, hip, inputs, min(args.warmup, 5))
 
+    blocks = None
+    if not args.no_blocks and w.name == "wan_21x30x52" and phi in ("elu1", "poly2"):
+        dense_attn = None
+        if dense is not None:
+            dense_attn = dense["ms_per_step"]
+        blocks = block_bench(rh, inputs, w, Tc, To, phi, max(3, args.steps // 4), main_t["ms_per_step"], dense_attn)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, Tc, To, phi, args.cpu_seconds)
@@ -489,6 +568,7 @@ def main():
         "backward": backward,
         "length_scaling": length,
         "other_workloads": sweep,
+        "attention_blocks": blocks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

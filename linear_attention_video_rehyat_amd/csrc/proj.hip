@@ -30,15 +30,30 @@ namespace rehyat {
 
 namespace {
 
-constexpr int kProjBF = 128;   // features per workgroup tile
-constexpr int kProjBT = 128;   // tokens per workgroup tile
 constexpr int kProjBK = 32;    // input features per LDS stage
-constexpr int kProjStages = 4;
-constexpr int kProjWaves = 4;
+constexpr int kProjMinBF = 128;
 
-template <int MODE>
-__global__ __launch_bounds__(kProjWaves * 64) void proj_bf16_kernel(ProjParams p) {
-    constexpr int BF = kProjBF, BT = kProjBT, BK = kProjBK, NS = kProjStages, NW = kProjWaves;
+// Tile configurations: workgroup tile BF features x BT tokens, NW waves in a
+// WGF x (NW / WGF) grid, each wave (BF / WGF) features x (BT * WGF / NW)
+// tokens, NS LDS stages.
+struct ProjCfg {
+    int BF, BT, NW, WGF, NS;
+};
+constexpr ProjCfg kProjCfgs[3] = {{128, 128, 4, 2, 4}, {256, 256, 8, 2, 3}, {256, 128, 8, 4, 4}};
+#ifndef REHYAT_PROJ_CFG
+#define REHYAT_PROJ_CFG 1
+#endif
+
+// The body, instantiated per (epilogue, configuration) and wrapped by one
+// kernel per configuration below (with the configuration as a second template
+// parameter of the kernel itself, its host stubs were not emitted).
+template <int MODE, int CFG>
+__device__ __forceinline__ void proj_body(const ProjParams& p) {
+    constexpr int BF = kProjCfgs[CFG].BF, BT = kProjCfgs[CFG].BT, NW = kProjCfgs[CFG].NW;
+    constexpr int WGF = kProjCfgs[CFG].WGF, NS = kProjCfgs[CFG].NS;
+    constexpr int BK = kProjBK;
+    constexpr int WGT = NW / WGF;
+    constexpr int MI = BF / WGF / 32, NJ = BT / WGT / 32;  // 32x32 MFMA tiles per wave
     constexpr int CK = BK / 8;                       // 16-byte chunks per tile row
     constexpr int WT = BF * BK, XT = BT * BK;        // elements per W / X tile
     constexpr int STAGE = WT + XT;
@@ -54,7 +69,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void proj_bf16_kernel(ProjParams p
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int lq = lane & 31;
-    const int wf = wave >> 1, wt = wave & 1;         // the wave's 64 features x 64 tokens
+    const int wf = wave / WGT, wt = wave % WGT;      // the wave's 32 MI features x 32 NJ tokens
 
     // tile order: feature tiles fastest, so the workgroups on an XCD share X rows
     const int nft = p.n_out / BF;
@@ -119,11 +134,11 @@ __global__ __launch_bounds__(kProjWaves * 64) void proj_bf16_kernel(ProjParams p
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
     const int nk = C / BK;
     for (int kt = 0; kt < NS - 1 && kt < nk; ++kt) issue(kt, smem + kt * STAGE);
@@ -138,32 +153,36 @@ __global__ __launch_bounds__(kProjWaves * 64) void proj_bf16_kernel(ProjParams p
         const lds_u16* Xs = Ws + WT;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
-            bf16x8 a[2], b[2];
+            bf16x8 a[MI], b[NJ];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int rw = 64 * wf + 32 * i + lq, rx = 64 * wt + 32 * i + lq;
+            for (int i = 0; i < MI; ++i) {
+                const int rw = 32 * (MI * wf + i) + lq;
                 a[i] = lds_read_b128(Ws, rw * BK + (((2 * s + h) ^ swz<CK>(rw)) << 3));
-                b[i] = lds_read_b128(Xs, rx * BK + (((2 * s + h) ^ swz<CK>(rx)) << 3));
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < NJ; ++j) {
+                const int rx = 32 * (NJ * wt + j) + lq;
+                b[j] = lds_read_b128(Xs, rx * BK + (((2 * s + h) ^ swz<CK>(rx)) << 3));
+            }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
         }
     }
 
-    // ---- epilogue: lane holds token t0 + 64 wt + 32 j + lq; register 4g + e is
-    // feature f0 + 64 wf + 32 i + 8 g + 4 h + e
+    // ---- epilogue: lane holds token t0 + 32 (NJ wt + j) + lq; register 4g + e is
+    // feature f0 + 32 (MI wf + i) + 8 g + 4 h + e
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int t = t0 + 64 * wt + 32 * j + lq;
+    for (int j = 0; j < NJ; ++j) {
+        const int t = t0 + 32 * (NJ * wt + j) + lq;
         if (t >= p.T) continue;
         const int b = t / p.N, n = t - (t / p.N) * p.N;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int f = f0 + 64 * wf + 32 * i + 8 * g + 4 * h;
+                const int f = f0 + 32 * (MI * wf + i) + 8 * g + 4 * h;
                 const f32x4 bias = *(const f32x4*)(p.bias + f);
                 float y[4];
 #pragma unroll
@@ -189,17 +208,35 @@ __global__ __launch_bounds__(kProjWaves * 64) void proj_bf16_kernel(ProjParams p
     }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(64 * 4) void proj_bf16_small_kernel(ProjParams p) {
+    proj_body<MODE, 0>(p);
+}
+template <int MODE>
+__global__ __launch_bounds__(64 * 8) void proj_bf16_kernel(ProjParams p) {
+    proj_body<MODE, REHYAT_PROJ_CFG>(p);
+}
+
 }  // namespace
 
 bool proj_shape_ok(int c_in, int n_out, int head_dim) {
-    return c_in % kProjBK == 0 && n_out % kProjBF == 0 && head_dim % kProjBK == 0 && c_in % head_dim == 0;
+    return c_in % kProjBK == 0 && n_out % kProjMinBF == 0 && head_dim % kProjBK == 0 && c_in % head_dim == 0;
 }
 
 hipError_t launch_proj_bf16(const ProjParams& p, hipStream_t s) {
-    const long long tiles = (long long)(p.n_out / kProjBF) * ((p.T + kProjBT - 1) / kProjBT);
+    // the larger tiles where the features split into them, else 128 x 128
+    const ProjCfg c = kProjCfgs[REHYAT_PROJ_CFG];
+    const bool big = REHYAT_PROJ_CFG != 0 && p.n_out % c.BF == 0;
+    const ProjCfg u = big ? c : kProjCfgs[0];
+    const long long tiles = (long long)(p.n_out / u.BF) * ((p.T + u.BT - 1) / u.BT);
     if (tiles <= 0) return hipSuccess;
-    if (p.mode == kProjQKV) proj_bf16_kernel<kProjQKV><<<(unsigned)tiles, kProjWaves * 64, 0, s>>>(p);
-    else proj_bf16_kernel<kProjOut><<<(unsigned)tiles, kProjWaves * 64, 0, s>>>(p);
+    if (big) {
+        if (p.mode == kProjQKV) proj_bf16_kernel<kProjQKV><<<(unsigned)tiles, u.NW * 64, 0, s>>>(p);
+        else proj_bf16_kernel<kProjOut><<<(unsigned)tiles, u.NW * 64, 0, s>>>(p);
+    } else {
+        if (p.mode == kProjQKV) proj_bf16_small_kernel<kProjQKV><<<(unsigned)tiles, u.NW * 64, 0, s>>>(p);
+        else proj_bf16_small_kernel<kProjOut><<<(unsigned)tiles, u.NW * 64, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 
