@@ -43,20 +43,28 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "354c466ab73a0a4a", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (259286 * 2.0 + 98290 * 1.0) * 1024}
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "ccf713e86574e8a3", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (251972.4 * 2.0 + 98280.5 * 1.0) * 1024}
 
 
-LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h", "kernels.h")
+LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h")
 
 
 def local_kernel_sha():
-    """Hash of the sources the local kernel is compiled from."""
+    """Hash of what the local kernel is compiled from: its sources and, from
+    kernels.h (which also declares every other kernel's parameters), the
+    LocalParams block and the helpers after it up to the block-state section."""
     import hashlib
     h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_video_rehyat_amd", "csrc")
     for name in LOCAL_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "linear_attention_video_rehyat_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "kernels.h"), "rb") as f:
+        text = f.read()
+    start = text.index(b"struct LocalParams {")
+    end = text.index(b"// Block-state pass:", start)
+    h.update(text[start:end])
     return h.hexdigest()[:16]
 
 
