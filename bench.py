@@ -238,8 +238,9 @@ def length_scaling_bench(rh, hip, inputs, warmup):
     """Forward time against clip length: the first F = 21, 42, ..., 105 latent
     frames (1560 tokens each) of the 105-frame workload, T_c = 3, T_o = 1,
     elu+1; least-squares line, its R^2, and the 105 frames again as 35
-    streaming steps of 3 frames (the chunk-wise RNN form), with the device
-    memory high-water of the streaming loop at 21 and at 105 frames."""
+    streaming steps of 3 frames (the chunk-wise RNN form; after a warm-up
+    stream, the mean of 5 streams run back to back), with the device memory
+    high-water of the streaming loop at 21 and at 105 frames."""
     import numpy as np
     import torch
     wl = inputs.WORKLOADS["wan_long_105x30x52"]
@@ -259,8 +260,9 @@ def length_scaling_bench(rh, hip, inputs, warmup):
     a, b = np.polyfit(x, y, 1)
     r2 = 1.0 - float(((y - (a * x + b)) ** 2).sum() / ((y - y.mean()) ** 2).sum())
 
-    def stream(F):
-        st = rh.StepState(1, wl.H, HW, wl.head_dim, 3, 1, "elu1")
+    def stream(F, reps=1):
+        # `reps` whole streams back to back (a fresh state each), mean time per stream
+        sts = [rh.StepState(1, wl.H, HW, wl.head_dim, 3, 1, "elu1") for _ in range(reps)]
         chunks = [tuple(x[:, :, 3 * i * HW:3 * (i + 1) * HW].contiguous() for x in (q, k, v))
                   for i in range(F // 3)]
         outs = [torch.empty_like(c[0]) for c in chunks]
@@ -268,18 +270,20 @@ def length_scaling_bench(rh, hip, inputs, warmup):
         torch.cuda.reset_peak_memory_stats()
         base = torch.cuda.memory_allocated()
         t0 = time.perf_counter()
-        for c, o in zip(chunks, outs):
-            st.step(*c, out=o)
+        for st in sts:
+            for c, o in zip(chunks, outs):
+                st.step(*c, out=o)
         torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        return dt, torch.cuda.max_memory_allocated() - base, st.nbytes
+        dt = (time.perf_counter() - t0) / reps
+        return dt, torch.cuda.max_memory_allocated() - base, sts[0].nbytes
 
-    stream(21)  # warm-up
-    dt105, hw105, sb105 = stream(105)
+    stream(105)  # warm-up, as the forwards above are timed after theirs
+    dt105, hw105, sb105 = stream(105, reps=5)
     _, hw21, sb21 = stream(21)
     return {"frames": frames, "ms_per_fwd": [round(m, 4) for m in ms],
             "slope_ms_per_21_frames": round(a * 21, 4), "intercept_ms": round(b, 4), "r2": round(r2, 5),
             "stream_105_frames": {"steps": 35, "ms": round(dt105 * 1000.0, 3),
+                                  "vs_one_shot_105": round(dt105 * 1000.0 / ms[-1], 3),
                                   "tokens_per_s": round(105 * HW / dt105, 1),
                                   "state_bytes": sb105, "state_bytes_at_21_frames": sb21,
                                   "extra_device_bytes_105": hw105, "extra_device_bytes_21": hw21}}

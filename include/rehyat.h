@@ -41,7 +41,14 @@
  *     while they queue their launches (each call holds its arena until its last
  *     launch is queued).  The arena of a stream lives until the process ends or
  *     rehyat_workspace_release() frees it; release it before destroying a stream
- *     that made calls.
+ *     that made calls.  A streaming step (rehyat_attn_step*) with a linear
+ *     branch queues the sums of the keys leaving its window on a library-owned
+ *     side stream of (device, stream), beside its local-attention kernel: the
+ *     side stream waits for an event recorded on `stream`, and `stream` waits
+ *     for an event recorded on the side stream before the rest of the step.
+ *     Work queued on `stream` afterwards is ordered after the whole step, as
+ *     for any other call, and graph capture of `stream` takes the side stream
+ *     in.  rehyat_workspace_release() destroys that side stream too.
  *   - Sizes: the rows of one (b, h) are addressed with 32-bit byte offsets, so
  *     frames * tokens_per_frame * (row bytes) must stay below 2^31, where a row
  *     is head_dim elements (2 head_dim with the learned maps); larger clips are
@@ -346,8 +353,9 @@ rehyat_status rehyat_set_profile_events(void* const* events, int n_events);
 
 /*
  * Waits for the work queued on `stream` (on the current device) and frees the
- * workspace arena of that stream.  The next call on the stream allocates a new
- * one.  Must not run concurrently with a call on the same stream.
+ * workspace arena of that stream and its side stream.  The next call on the
+ * stream allocates new ones.  Must not run concurrently with a call on the same
+ * stream.
  */
 rehyat_status rehyat_workspace_release(void* stream);
 

@@ -298,6 +298,78 @@ rehyat_status arena_release(hipStream_t s) {
     return REHYAT_OK;
 }
 
+// Side streams.  A streaming step's local-attention launch covers one chunk
+// (228 workgroups at the Wan shape, fewer than the 256 CUs), and the state
+// update that the next step needs (fold, scan, overlap copy) reads only the
+// step's inputs, so it runs beside the local launch on a library-owned stream:
+// an event recorded on the caller's stream forks it, an event recorded on it
+// joins the caller's stream back.  One per (device, caller stream), created on
+// first use and kept until rehyat_workspace_release for that stream; its lock
+// is held while a call queues work on it.
+struct SideStream {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_sides_mu;
+std::map<std::pair<int, uintptr_t>, std::unique_ptr<SideStream>> g_sides;
+
+struct SideLease {
+    std::unique_lock<std::mutex> lock;
+    SideStream* side = nullptr;
+};
+
+void side_destroy(SideStream& ss) {
+    if (ss.s) (void)hipStreamSynchronize(ss.s);
+    if (ss.join) (void)hipEventDestroy(ss.join);
+    if (ss.fork) (void)hipEventDestroy(ss.fork);
+    if (ss.s) (void)hipStreamDestroy(ss.s);
+    ss.s = nullptr;
+    ss.fork = ss.join = nullptr;
+}
+
+rehyat_status side_acquire(hipStream_t s, SideLease& lease) {
+    int dev = 0;
+    hipError_t e = hip_step([&] { return hipGetDevice(&dev); });
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    SideStream* ss = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_sides_mu);
+        std::unique_ptr<SideStream>& slot = g_sides[{dev, (uintptr_t)s}];
+        if (!slot) slot.reset(new SideStream());
+        ss = slot.get();
+    }
+    std::unique_lock<std::mutex> lock(ss->mu);
+    if (!ss->s) {
+        e = hip_step([&] { return hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking); });
+        if (e == hipSuccess) e = hip_step([&] { return hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming); });
+        if (e == hipSuccess) e = hip_step([&] { return hipEventCreateWithFlags(&ss->join, hipEventDisableTiming); });
+        if (e != hipSuccess) {
+            side_destroy(*ss);
+            return hip_fail(e, "side stream creation");
+        }
+    }
+    lease.side = ss;
+    lease.lock = std::move(lock);
+    return REHYAT_OK;
+}
+
+// Waits for the side stream's work and destroys it (current device).
+void side_release(hipStream_t s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    std::unique_ptr<SideStream> ss;
+    {
+        std::lock_guard<std::mutex> lock(g_sides_mu);
+        auto it = g_sides.find({dev, (uintptr_t)s});
+        if (it == g_sides.end()) return;
+        std::lock_guard<std::mutex> slock(it->second->mu);
+        ss = std::move(it->second);
+        g_sides.erase(it);
+    }
+    side_destroy(*ss);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of the whole-clip forward: partial block sums and prepared states.
@@ -995,10 +1067,39 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
     char* base = (char*)st->buf;
     const int P = st->prev_frames * g.HW;
     const int cur = st->prev_slot;
+    const long long done = st->frames_done + frames;
+    const int keep_frames = (int)std::min<long long>(g.To, done);
+    const int keep_rows = keep_frames * g.HW;
+    const int evict_rows = P + (int)n - keep_rows;
+    const bool fold = g.phi != REHYAT_PHI_NONE && evict_rows > 0;
+    const bool copy = keep_rows > 0;
+    const SubSplit split = state_split(g.dtype, std::max(evict_rows, 1));
+    if (split.n_sub > L.n_sub) return fail(REHYAT_EINVAL, "internal: state split exceeds its buffer");
     if (mlp) {  // phi of the chunk's queries and keys (the overlap frames' phi(k) is carried)
         hipError_t e = hip_step([&] { return launch_mlp(g, wq, wk, q, base + L.fq_off, n, 0, (int)n, k, base + L.fk_off, n, 0, (int)n, s); });
         if (e != hipSuccess) return hip_fail(e, "feature-map launch");
     }
+
+    // the side stream forks here (after the inputs and the chunk's features)
+    SideLease side;
+    hipStream_t a = s;
+    if (fold) {
+        rehyat_status ss = side_acquire(s, side);
+        if (ss != REHYAT_OK) return ss;
+        a = side.side->s;
+        hipError_t e = hip_step([&] { return hipEventRecord(side.side->fork, s); });
+        if (e != hipSuccess) return hip_fail(e, "fork event");
+    }
+    bool forked = false;
+    // after the side stream waited for the fork, a failure still joins it back,
+    // so that nothing the call queued outlives it unordered
+    auto failed = [&](hipError_t e, const char* what) {
+        if (forked) {
+            if (hipEventRecord(side.side->join, a) != hipSuccess || hipStreamWaitEvent(s, side.side->join, 0) != hipSuccess)
+                (void)hipStreamSynchronize(a);
+        }
+        return hip_fail(e, what);
+    };
 
     // 1. local softmax over [prev | chunk] + linear branch from the carried state
     LocalParams lp{};
@@ -1022,22 +1123,25 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
         lp.fq = base + L.fq_off;
         lp.fq_bh_stride = n * g.Dp;
     }
+    // queued first, so that its workgroups take the CUs before the side stream's
     hipError_t e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_local_bf16(lp, s) : launch_local_f32(lp, s); });
-    if (e != hipSuccess) return hip_fail(e, "local-attention launch");
+    if (e != hipSuccess) return failed(e, "local-attention launch");
+    if (fold) {
+        e = hip_step([&] { return hipStreamWaitEvent(a, side.side->fork, 0); });
+        if (e != hipSuccess) return failed(e, "side stream wait");
+        forked = true;
+    }
 
-    // 2. fold the rows leaving the window into (S, z)
-    const long long done = st->frames_done + frames;
-    const int keep_frames = (int)std::min<long long>(g.To, done);
-    const int keep_rows = keep_frames * g.HW;
-    const int evict_rows = P + (int)n - keep_rows;
-    bool nonempty = st->state_nonempty != 0;
-    if (g.phi != REHYAT_PHI_NONE && evict_rows > 0) {
-        StateParams sp{};
+    // 2. on the side stream: the sums of the rows leaving the window (fold).
+    // They share the GPU with this step's local launch, so the fold uses at
+    // most one workgroup per CU that launch leaves idle, each taking several
+    // sub-blocks in turn: a workgroup sent to a shader engine with no idle CU
+    // would wait for the local launch to end.
+    StateParams sp{};
+    if (fold) {
         sp.k = k; sp.v = v; sp.kp = lp.kp; sp.vp = lp.vp;
         sp.bh_stride = n * g.d; sp.prev_bh_stride = lp.prev_bh_stride; sp.prev_rows = P;
         sp.HW = g.HW; sp.Tc = g.Tc; sp.To = g.To;
-        const SubSplit split = state_split(g.dtype, evict_rows);
-        if (split.n_sub > L.n_sub) return fail(REHYAT_EINVAL, "internal: state split exceeds its buffer");
         sp.n_blocks = 1; sp.sub_rows = split.sub_rows;
         sp.n_sub = split.n_sub;
         sp.stream_rows = evict_rows;
@@ -1049,9 +1153,27 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
             sp.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; sp.fkp_bh_stride = (long long)g.To * g.HW * g.Dp;
         }
         sp.items_per_bh = state_items_per_bh(sp);
-        e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, s) : launch_state_f32(sp, s); });
-        if (e != hipSuccess) return hip_fail(e, "block-state launch");
-        ScanParams cp{};
+        const int idle = cus_per_xcd() * 8 - lp.tiles_per_chunk * lp.BH;
+        const int items = sp.items_per_bh * g.BH;
+        if (idle > 0 && items > idle) sp.wg_items = (items + idle - 1) / idle;
+        e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, a) : launch_state_f32(sp, a); });
+        if (e != hipSuccess) return failed(e, "block-state launch");
+        e = hip_step([&] { return hipEventRecord(side.side->join, a); });
+        if (e != hipSuccess) return failed(e, "join event");
+        e = hip_step([&] { return hipStreamWaitEvent(s, side.side->join, 0); });
+        if (e != hipSuccess) {
+            (void)hipStreamSynchronize(a);
+            return hip_fail(e, "join wait");
+        }
+        forked = false;
+    }
+    // 3. after the local launch (which reads the prepared state and the K/V
+    // slot), on the caller's stream, in one launch: add the fold into (S, z)
+    // and prepare it for the next step; keep the last min(T_o, frames so far)
+    // frames for the next window in the other K/V slot
+    bool nonempty = st->state_nonempty != 0;
+    ScanParams cp{};
+    if (fold) {
         cp.partial = sp.partial; cp.part = state_part(sp);
         cp.init = nonempty ? (const float*)(base + L.S_off) : nullptr;
         cp.state_out = (float*)(base + L.S_off);
@@ -1061,13 +1183,10 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
         cp.U = 1; cp.n_sub = sp.n_sub; cp.BH = g.BH; cp.d = g.d; cp.Dp = g.Dp;
         cp.t_first = 1; cp.t_offset = 1; cp.f32_prep = g.dtype == REHYAT_F32;
         cp.mode = kCausal; cp.C = 1; cp.q = 0; cp.suffix = nullptr;
-        e = hip_step([&] { return launch_scan(cp, s); });
-        if (e != hipSuccess) return hip_fail(e, "scan launch");
         nonempty = true;
     }
-    // 3. keep the last min(T_o, frames so far) frames for the next window
-    if (keep_rows > 0) {
-        PrevCopyParams pc{};
+    PrevCopyParams pc{};
+    if (copy) {
         pc.kp = lp.kp; pc.vp = lp.vp; pc.prev_bh_stride = lp.prev_bh_stride; pc.prev_rows = P;
         pc.k = k; pc.v = v; pc.bh_stride = n * g.d; pc.chunk_rows = (int)n;
         pc.kd = base + L.kp_off[cur ^ 1]; pc.vd = base + L.vp_off[cur ^ 1];
@@ -1076,10 +1195,12 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
             pc.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; pc.fk = base + L.fk_off; pc.fkd = base + L.fkp_off[cur ^ 1];
             pc.fprev_bh_stride = (long long)g.To * g.HW * g.Dp; pc.f_bh_stride = n * g.Dp; pc.f_cols = g.Dp;
         }
-        e = hip_step([&] { return launch_prev_copy(pc, s); });
-        if (e != hipSuccess) return hip_fail(e, "overlap copy launch");
     }
-    st->prev_slot = keep_rows > 0 ? cur ^ 1 : cur;
+    if (fold || copy) {
+        e = hip_step([&] { return launch_scan_copy(fold ? &cp : nullptr, copy ? &pc : nullptr, s); });
+        if (e != hipSuccess) return hip_fail(e, "state update launch");
+    }
+    st->prev_slot = copy ? cur ^ 1 : cur;
     st->prev_frames = keep_frames;
     st->state_nonempty = nonempty ? 1 : 0;
     st->frames_done = done;
@@ -1186,6 +1307,7 @@ rehyat_status rehyat_feature_mlp(const void* x, void* phi, int dtype, int B, int
 
 rehyat_status rehyat_workspace_release(void* stream) {
     begin_call();
+    side_release((hipStream_t)stream);
     return arena_release((hipStream_t)stream);
 }
 

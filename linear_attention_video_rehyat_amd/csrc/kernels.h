@@ -175,6 +175,9 @@ struct StateParams {
     // backward (kChunkRows): row r contributes c_r phi(x_r) v_r^T to S and
     // D_r c_r phi(x_r) to z, c_r = exp(-row_lse[r]), D_r = row_d[r] ([BH][n_rows])
     const float* row_lse; const float* row_d;
+    // bf16 elu+1 / poly2: sub-blocks per workgroup (0 or 1: one workgroup each);
+    // more: fewer workgroups take the sub-blocks in turn (same results)
+    int wg_items;
 };
 
 // The blocks of a state partition and their sub-blocks: block u covers rows
@@ -311,6 +314,8 @@ hipError_t launch_state_bf16(const StateParams& p, hipStream_t s);
 hipError_t launch_state_f32(const StateParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s);
+// scan and copy in one launch (either may be null)
+hipError_t launch_scan_copy(const ScanParams* sp, const PrevCopyParams* pc, hipStream_t s);
 hipError_t launch_phi_mlp_bf16(const MlpParams& p, hipStream_t s);
 hipError_t launch_bwd_dsum(const BwdParams& p, float* dsum, bool bf16, hipStream_t s);  // dsum = rowwise dy . out
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);   // dq, dk, dv

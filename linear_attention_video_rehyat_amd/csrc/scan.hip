@@ -17,11 +17,9 @@ namespace rehyat {
 
 namespace {
 
-__global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
+// Elements e4 .. e4+3 of the state of (b, h) bh.
+__device__ __forceinline__ void scan_elem(const ScanParams& p, const int bh, const int e4) {
     const int E = p.d * p.Dp + p.Dp;
-    const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
-    const int bh = blockIdx.y;
-    if (e4 >= E) return;
     const long long pstride = (long long)E;  // between sub-blocks
     const float* part = p.partial + (long long)bh * p.U * p.n_sub * E + e4;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -220,12 +218,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
     if (p.state_out) *(f32x4*)(p.state_out + (long long)bh * E + e4) = x;
 }
 
-__global__ __launch_bounds__(256) void prev_copy_kernel(PrevCopyParams p) {
-    // 16-byte chunks of one row: d * elem_bytes / 16
-    const int cpr = p.d * p.elem_bytes / 16;
-    const long long total = (long long)p.BH * p.keep_rows * cpr;
-    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total) return;
+__global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
+    const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e4 >= p.d * p.Dp + p.Dp) return;
+    scan_elem(p, blockIdx.y, e4);
+}
+
+// 16-byte chunk idx of the kept rows (chunks of a row: d * elem_bytes / 16).
+__device__ __forceinline__ void prev_copy_chunk(const PrevCopyParams& p, const int cpr, const long long idx) {
     const int c = (int)(idx % cpr);
     const long long rr = idx / cpr;
     const int r = (int)(rr % p.keep_rows);
@@ -246,6 +246,29 @@ __global__ __launch_bounds__(256) void prev_copy_kernel(PrevCopyParams p) {
     if (p.vd) *(u32x4*)((char*)p.vd + doff) = *(const u32x4*)(vs + 16LL * c);
 }
 
+__global__ __launch_bounds__(256) void prev_copy_kernel(PrevCopyParams p) {
+    const int cpr = p.d * p.elem_bytes / 16;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.BH * p.keep_rows * cpr) return;
+    prev_copy_chunk(p, cpr, idx);
+}
+
+// A streaming step's update after its local launch, in one launch: the first
+// scan_blocks workgroups add the fold into the state (as scan_kernel, the
+// blocks of each (b, h) in turn), the others copy the kept rows.
+__global__ __launch_bounds__(256) void scan_copy_kernel(ScanParams sp, PrevCopyParams pc, int scan_blocks) {
+    if ((int)blockIdx.x < scan_blocks) {
+        const int E = sp.d * sp.Dp + sp.Dp;
+        const int bx = (E / 4 + 255) / 256;
+        const int e4 = ((blockIdx.x % bx) * 256 + threadIdx.x) * 4;
+        if (e4 < E) scan_elem(sp, blockIdx.x / bx, e4);
+        return;
+    }
+    const int cpr = pc.d * pc.elem_bytes / 16;
+    const long long idx = (long long)(blockIdx.x - scan_blocks) * 256 + threadIdx.x;
+    if (idx < (long long)pc.BH * pc.keep_rows * cpr) prev_copy_chunk(pc, cpr, idx);
+}
+
 }  // namespace
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
@@ -256,19 +279,39 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s) {
-    const long long total = (long long)p.BH * p.keep_rows * (p.d * p.elem_bytes / 16);
-    if (total <= 0) return hipSuccess;
-    const long long blocks = (total + 255) / 256;
-    prev_copy_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(p);
-    if (!p.fkd) return hipGetLastError();
-    // the phi(K) rows of the same frames, as a plane of their own
+namespace {
+long long copy_chunks(const PrevCopyParams& p) { return (long long)p.BH * p.keep_rows * (p.d * p.elem_bytes / 16); }
+
+void prev_copy_plane(const PrevCopyParams& p, hipStream_t s) {
+    const long long total = copy_chunks(p);
+    if (total > 0) prev_copy_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, s>>>(p);
+}
+
+// the phi(K) rows of the same frames, as a plane of their own
+PrevCopyParams feature_plane(const PrevCopyParams& p) {
     PrevCopyParams f = p;
     f.kp = p.fkp; f.k = p.fk; f.kd = p.fkd;
     f.vp = nullptr; f.v = nullptr; f.vd = nullptr;
     f.prev_bh_stride = p.fprev_bh_stride; f.bh_stride = p.f_bh_stride; f.d = p.f_cols;
-    const long long ftotal = (long long)p.BH * p.keep_rows * (f.d * p.elem_bytes / 16);
-    prev_copy_kernel<<<dim3((unsigned)((ftotal + 255) / 256)), 256, 0, s>>>(f);
+    return f;
+}
+}  // namespace
+
+hipError_t launch_prev_copy(const PrevCopyParams& p, hipStream_t s) {
+    prev_copy_plane(p, s);
+    if (p.fkd) prev_copy_plane(feature_plane(p), s);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_copy(const ScanParams* sp, const PrevCopyParams* pc, hipStream_t s) {
+    if (!sp) return pc ? launch_prev_copy(*pc, s) : hipSuccess;
+    if (!pc) return launch_scan(*sp, s);
+    const int E = sp->d * sp->Dp + sp->Dp;
+    const long long scan_blocks = (long long)((E / 4 + 255) / 256) * sp->BH;
+    const long long copy_blocks = (copy_chunks(*pc) + 255) / 256;
+    if (scan_blocks + copy_blocks > 0)
+        scan_copy_kernel<<<dim3((unsigned)(scan_blocks + copy_blocks)), 256, 0, s>>>(*sp, *pc, (int)scan_blocks);
+    if (pc->fkd) prev_copy_plane(feature_plane(*pc), s);
     return hipGetLastError();
 }
 

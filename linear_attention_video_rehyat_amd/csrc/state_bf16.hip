@@ -96,8 +96,9 @@ constexpr int state_nw(int d, int phi) {
 
 // GRAD: the backward's gradient sums (rows are queries of a chunk, the second
 // operand is dy; row r's phi is scaled by exp(-lse_r) and its z weight is dsum_r)
-template <int D, int PHI, bool GRAD = false>
-__global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(StateParams p) {
+// One sub-block (work item) of the partition: its partial sums.
+template <int D, int PHI, bool GRAD>
+__device__ __forceinline__ void state_item(const StateParams& p, const int item) {
     constexpr bool FEAT = PHI == kPhiFeat;            // phi(k) rows come precomputed
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     constexpr int KW = FEAT ? DP : D;                 // columns of the K tile
@@ -119,7 +120,10 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
     static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
     static_assert(!GRAD || BN == 64, "one 4-byte-per-lane load carries a tile's lse (and one its dsum)");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem_raw[NS * STAGE];
+    // the ring, reused at the end for the sums of the waves that share a feature tile
+    constexpr int RED_U16 = SPLIT > 1 ? 2 * ((SPLIT - 1) * NT * DT * 16 * 64 + (SPLIT - 1) * NT * 32) : 0;
+    constexpr int SMEM_U16 = NS * STAGE > RED_U16 ? NS * STAGE : RED_U16;
+    __shared__ __attribute__((aligned(16))) uint16_t smem_raw[SMEM_U16];
     lds_u16* const smem = (lds_u16*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -130,9 +134,7 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
     const int nt0 = wave % (NT >= NW ? NW : NT);      // first feature tile of the wave
     const int kpart = wave / (NT >= NW ? NW : NT);    // which share of the 16-key steps
 
-    // block -> (bh, u, sub): the sub-blocks of a (b, h), block by block (only
-    // the workgroups with work are launched)
-    const int item = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    // item -> (bh, u, sub): the sub-blocks of a (b, h), block by block
     const int bh = item / p.items_per_bh;
     int sub = item - bh * p.items_per_bh;
     const BlockPart part = state_part(p);
@@ -372,17 +374,40 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(State
     }
 }
 
+// One workgroup per sub-block, in the XCD-aware order (only the workgroups
+// with work are launched).
+template <int D, int PHI, bool GRAD = false>
+__global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_kernel(StateParams p) {
+    state_item<D, PHI, GRAD>(p, __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x)));
+}
+
+// A few workgroups taking the sub-blocks in turn (the streaming fold, which
+// runs beside a local-attention launch on the CUs that launch leaves idle: one
+// workgroup per idle CU, so that none waits for a CU the local launch holds).
+// Each sub-block's partial is computed exactly as above.
+template <int D, int PHI>
+__global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_multi_kernel(StateParams p) {
+    const int n = p.BH * p.items_per_bh;
+    for (int item = blockIdx.x; item < n; item += gridDim.x) {
+        state_item<D, PHI, false>(p, item);
+        __syncthreads();  // the next item refills the ring
+    }
+}
+
 template <int D>
 hipError_t launch_d(const StateParams& p, hipStream_t s) {
-    const long long blocks = (long long)p.BH * p.items_per_bh;
-    if (blocks <= 0) return hipSuccess;
+    const long long items = (long long)p.BH * p.items_per_bh;
+    if (items <= 0) return hipSuccess;
+    const long long blocks = p.wg_items > 1 ? (items + p.wg_items - 1) / p.wg_items : items;
     switch (p.phi) {
     case kPhiElu1:
         if (p.row_lse) state_bf16_kernel<D, kPhiElu1, true><<<(unsigned)blocks, state_nw(D, kPhiElu1) * 64, 0, s>>>(p);
+        else if (p.wg_items > 1) state_bf16_multi_kernel<D, kPhiElu1><<<(unsigned)blocks, state_nw(D, kPhiElu1) * 64, 0, s>>>(p);
         else state_bf16_kernel<D, kPhiElu1><<<(unsigned)blocks, state_nw(D, kPhiElu1) * 64, 0, s>>>(p);
         break;
     case kPhiPoly2:
         if (p.row_lse) state_bf16_kernel<D, kPhiPoly2, true><<<(unsigned)blocks, state_nw(D, kPhiPoly2) * 64, 0, s>>>(p);
+        else if (p.wg_items > 1) state_bf16_multi_kernel<D, kPhiPoly2><<<(unsigned)blocks, state_nw(D, kPhiPoly2) * 64, 0, s>>>(p);
         else state_bf16_kernel<D, kPhiPoly2><<<(unsigned)blocks, state_nw(D, kPhiPoly2) * 64, 0, s>>>(p);
         break;
     case kPhiFeat: state_bf16_kernel<D, kPhiFeat><<<(unsigned)blocks, state_nw(D, kPhiFeat) * 64, 0, s>>>(p); break;

@@ -22,6 +22,7 @@ hipError_t launch_state_bf16(const StateParams&, hipStream_t) { ++g_launches; re
 hipError_t launch_state_f32(const StateParams&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_scan(const ScanParams&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prev_copy(const PrevCopyParams&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_scan_copy(const ScanParams*, const PrevCopyParams*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_phi_mlp_bf16(const MlpParams&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_phi_mlp_f32(const MlpParams&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_bwd_dsum(const BwdParams&, float*, bool, hipStream_t) { ++g_launches; return hipSuccess; }

@@ -207,6 +207,39 @@ def test_injected_failure_backward_and_step():
     assert torch.equal(torch.cat(outs, dim=2), y_fwd)
 
 
+def test_injected_failure_at_every_step_of_a_streaming_step():
+    """A streaming step failed at each of its HIP steps in turn (the fork, the
+    local launch, the side stream's wait and launches, the join): REHYAT_EHIP
+    with the header unchanged; restoring the checkpoint taken before it then
+    continues the stream to the whole-clip forward's bits."""
+    g = (1, 2, 10, 100, 128, 3, 1)
+    B, H, F, HW, d, Tc, To = g
+    w = inputs.custom(*g, dtype="bf16", seed_id=762)
+    q, k, v = gpu(*inputs.make_qkv(w))
+    y_fwd = rh.attn_fwd(q, k, v, F, HW, Tc, To, "elu1")
+    chunks = []
+    for f in range(0, F, Tc):
+        sl = slice(f * HW, min(f + Tc, F) * HW)
+        chunks.append([t[:, :, sl].contiguous() for t in (q, k, v)])
+    st = rh.StepState(B, H, HW, d, Tc, To, "elu1")
+    outs = [st.step(*chunks[0]), st.step(*chunks[1])]
+    n_steps = rh.debug_hip_steps()
+    assert n_steps >= 8  # fork, local launch, side wait, state, scan, copy, join record and wait
+    sync()
+    saved = st.save()
+    for i in range(n_steps):
+        rh.debug_inject_hip_error(i)
+        with pytest.raises(rh.RehyatError, match=f"HIP step {i}"):
+            st.step(*chunks[2])
+        assert st.header() == saved[1]
+        sync()
+        st.restore(saved)
+    for c in chunks[2:]:
+        outs.append(st.step(*c))
+    sync()
+    assert torch.equal(torch.cat(outs, dim=2), y_fwd)
+
+
 def test_two_streams_concurrently():
     """Two different clips on two streams at once: each stream has its own
     workspace, so each result equals its single-stream run bit for bit."""

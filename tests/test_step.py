@@ -140,3 +140,30 @@ def test_long_105_frames_stream_vs_fwd_and_oracle():
                       "elu1", rows=rows)
     ys = to64(y_st[:, :, torch.from_numpy(rows).to("cuda")])
     check_bf16(ys, ref, "long 105-frame stream")
+
+
+def test_streams_on_two_user_streams_interleaved():
+    """Two streams of steps queued alternately on two user streams (each with
+    its own side stream for the fold, running concurrently): each equals its
+    whole-clip forward bit for bit; releasing a stream's workspace (and side
+    stream) in the middle of its stream changes nothing."""
+    g = (1, 3, 10, 150, 128, 3, 1)
+    B, H, F, HW, d, Tc, To = g
+    clips = [gpu(*inputs.make_qkv(inputs.custom(*g, dtype="bf16", seed_id=s))) for s in (531, 532)]
+    refs = [rh.attn_fwd(q, k, v, F, HW, Tc, To, "elu1") for q, k, v in clips]
+    sync()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    states = [rh.StepState(B, H, HW, d, Tc, To, "elu1") for _ in clips]
+    chunks = [[[t[:, :, f * HW:min(f + Tc, F) * HW].contiguous() for t in c] for f in range(0, F, Tc)] for c in clips]
+    sync()
+    outs = [[], []]
+    for i in range(len(chunks[0])):
+        for j in (0, 1):
+            with torch.cuda.stream(streams[j]):
+                outs[j].append(states[j].step(*chunks[j][i], stream=streams[j]))
+        if i == 1:
+            rh.workspace_release(streams[0])
+    sync()
+    for j in (0, 1):
+        assert torch.equal(torch.cat(outs[j], dim=2), refs[j]), j
+    rh.workspace_release(streams[1])
