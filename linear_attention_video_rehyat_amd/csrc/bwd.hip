@@ -568,7 +568,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
     const int rb = D * 2;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbp, (short)0, nkeys * rb, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbp, (short)0, nkeys * rb, 0x00020000);
-    auto load_tile = [&](int buf, int it) {
+    auto load_tile = [&](lds_u16* dst, int it) {
 #pragma unroll
         for (int o = 0; o < OPW; ++o) {
             const int op = wave + o * NW;
@@ -578,8 +578,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
             const int r = pos / C;
             const int off = (it * BN + r) * rb + ((pos % C) ^ swz<C>(r)) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs,
-                                                     (__attribute__((address_space(3))) void*)(
-                                                         (lds_u16*)tiles_raw[buf] + (isv ? KT : 0) + 512 * ins),
+                                                     (__attribute__((address_space(3))) void*)(dst + (isv ? KT : 0) + 512 * ins),
                                                      16, off, 0, 0, 0);
         }
     };
@@ -605,8 +604,10 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
         const int buf = it & 1;
         __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         lds_barrier();
-        if (it + 1 < ntiles) load_tile(buf ^ 1, it + 1);
-        const lds_u16* Ks = (const lds_u16*)tiles_raw[buf];
+        // the slot being filled and the slot being read never overlap; as
+        // restrict pointers they keep the reads clear of a wait for the loads
+        auto body = [&](lds_u16* __restrict__ fill, const lds_u16* __restrict__ Ks) {
+        if (it + 1 < ntiles) load_tile(fill, it + 1);
         const lds_u16* Vs = Ks + KT;
         // the S^T and dP^T chains of every 32-key subtile side by side
         constexpr int NKS = BN / 32;
@@ -651,8 +652,10 @@ __global__ __launch_bounds__(kBwdQWaves * 64) void dq_bf16_kernel(BwdParams p, i
                 }
             }
         }
+        };
+        body((lds_u16*)tiles_raw[buf ^ 1], (const lds_u16*)tiles_raw[buf]);
     };
-    if (ntiles > 0) load_tile(0, 0);
+    if (ntiles > 0) load_tile((lds_u16*)tiles_raw[0], 0);
     for (int it = 0; it < ntiles - 1; ++it) tile_step(std::false_type{}, it);
     if (ntiles > 0) tile_step(std::true_type{}, ntiles - 1);
 

@@ -87,8 +87,18 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
     const int b_end = (int)(total * (g + 1) / gridDim.x);
     if (b_begin >= b_end) return;
 
-    // one wave's share of the direct loads of an x block (swizzled rows)
-    auto load_x = [&](lds_u16* dst, int b) {
+    // one wave's share of an x block (swizzled rows): loaded into registers
+    // (xr) and written to the LDS slot later.  The per-lane byte offsets within
+    // a block are fixed; the block's first row goes in the scalar offset.
+    int xoff[OPW];
+#pragma unroll
+    for (int o = 0; o < OPW; ++o) {
+        const int pos = 64 * (wave + o * NW) + lane;
+        const int r = pos / C;
+        xoff[o] = r * D * 2 + ((pos % C) ^ swz<C>(r)) * 16;
+    }
+    u32x4 xr[OPW];
+    auto fetch_x = [&](int b) {
         int side, bh, row0;
         mlp_block(p, nb0, nb1, b, side, bh, row0);
         const MlpSide& sd = p.side[side];
@@ -96,21 +106,21 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)xb, (short)0, (sd.r1 - sd.r0) * D * 2, 0x00020000);  // rows past r1 read as zero
 #pragma unroll
-        for (int o = 0; o < OPW; ++o) {
-            const int ins = wave + o * NW;
-            const int pos = 64 * ins + lane;
-            const int r = pos / C;
-            const int off = (row0 + r) * D * 2 + ((pos % C) ^ swz<C>(r)) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * ins),
-                                                     16, off, 0, 0, 0);
-        }
+        for (int o = 0; o < OPW; ++o)
+            xr[o] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, xoff[o], row0 * D * 2, 0));
+    };
+    auto store_x = [&](lds_u16* dst) {
+#pragma unroll
+        for (int o = 0; o < OPW; ++o)
+            *(__attribute__((address_space(3))) u32x4*)(dst + 512 * (wave + o * NW) + 8 * lane) = xr[o];
     };
 
     bf16x8 w1f[KS1], w2f[KS2];
     float b1v[16], b2v[16];
     int loaded = -1;  // (side, head) whose weights the registers hold
 
-    load_x(xs, b_begin);
+    fetch_x(b_begin);
+    store_x(xs);
     for (int b = b_begin; b < b_end; ++b) {
         int side, bh, row0;
         mlp_block(p, nb0, nb1, b, side, bh, row0);
@@ -143,13 +153,17 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
                     for (int i = 0; i < 4; ++i) b2v[4 * j + i] = t[i];
                 }
             }
+            // the weights are in registers on every path below, so the
+            // compiler adds no waits for them
+            __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         }
-        // this block's x has landed (and every wave is done with the hidden
-        // tile and the x slot refilled next); then start the next block's x
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        // this block's x is in its LDS slot (and every wave is done with the
+        // hidden tile and with the x slot written next); the next block's x
+        // goes to registers now, to LDS after layer 2
         lds_barrier();
+        if (b + 1 < b_end) fetch_x(b + 1);
+        {
         const lds_u16* xcur = xs + ((b - b_begin) & 1) * XT;
-        if (b + 1 < b_end) load_x(xs + ((b + 1 - b_begin) & 1) * XT, b + 1);
 
         // layer 1: H^T rows [32 wave, +32) for 4 row tiles
         if (wave < HT) {
@@ -173,12 +187,16 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
                 }
             }
         }
+        }
         lds_barrier();
 
-        // layer 2: psi^T rows [32 wave, +32), phi, store
+        // layer 2: psi^T rows [32 wave, +32), phi, store (a resource ending at
+        // the side's last row drops the rows past it)
         if (wave < FT) {
-            const int nrows = sd.r1 - sd.r0 - row0;
+            const int nrows = min(sd.r1 - sd.r0 - row0, RB);
             uint16_t* ob = (uint16_t*)sd.out + bh * sd.out_bh_stride + (long long)(sd.r0 + row0) * 2 * D;
+            const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)ob, (short)0, nrows * 2 * D * 2, 0x00020000);
 #pragma unroll
             for (int rt = 0; rt < RB / 32; ++rt) {
                 const int row = 32 * rt + lq;
@@ -188,20 +206,24 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
                     const bf16x8 hf = lds_read_b128(hs, row * HID + (((2 * s + h) ^ hswz<CH>(row)) << 3));
                     acc = mfma32x32x16(w2f[s], hf, acc);
                 }
-                if (row < nrows) {
+                // the next block's x into its slot before the first phi store:
+                // the compiler's wait for the x registers would otherwise
+                // include the stores issued after the loads
+                if (rt == 0 && b + 1 < b_end) store_x(xs + ((b + 1 - b_begin) & 1) * XT);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float y[4];
+                for (int j = 0; j < 4; ++j) {
+                    float y[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float ps = acc[4 * j + i] + b2v[4 * j + i];
-                            y[i] = wave < FT / 2 ? elu1(ps) : ps * ps;
-                        }
-                        *(u32x2*)(ob + (long long)row * 2 * D + 32 * wave + 8 * j + 4 * h) =
-                            u32x2{pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
+                    for (int i = 0; i < 4; ++i) {
+                        const float ps = acc[4 * j + i] + b2v[4 * j + i];
+                        y[i] = wave < FT / 2 ? elu1(ps) : ps * ps;
                     }
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])}, ors,
+                                                          (row * 2 * D + 32 * wave + 8 * j + 4 * h) * 2, 0, 0);
                 }
             }
+        } else if (b + 1 < b_end) {
+            store_x(xs + ((b + 1 - b_begin) & 1) * XT);
         }
     }
 }
