@@ -239,8 +239,9 @@ def length_scaling_bench(rh, hip, inputs, warmup):
     frames (1560 tokens each) of the 105-frame workload, T_c = 3, T_o = 1,
     elu+1; least-squares line, its R^2, and the 105 frames again as 35
     streaming steps of 3 frames (the chunk-wise RNN form; after a warm-up
-    stream, the mean of 5 streams run back to back), with the device memory
-    high-water of the streaming loop at 21 and at 105 frames."""
+    stream, the mean of 5 streams run back to back; and the same 35 steps
+    captured in a HIP graph, replayed), with the device memory high-water of the
+    streaming loop at 21 and at 105 frames."""
     import numpy as np
     import torch
     wl = inputs.WORKLOADS["wan_long_105x30x52"]
@@ -280,10 +281,41 @@ def length_scaling_bench(rh, hip, inputs, warmup):
     stream(105)  # warm-up, as the forwards above are timed after theirs
     dt105, hw105, sb105 = stream(105, reps=5)
     _, hw21, sb21 = stream(21)
+
+    def stream_graph(reps=5):
+        # the 35 steps of a stream captured once in a HIP graph (from a fresh
+        # state, whose buffer needs no initialisation) and replayed as whole streams
+        chunks = [tuple(x[:, :, 3 * i * HW:3 * (i + 1) * HW].contiguous() for x in (q, k, v)) for i in range(35)]
+        outs = [torch.empty_like(c[0]) for c in chunks]
+        s = torch.cuda.Stream()
+        warm = rh.StepState(1, wl.H, HW, wl.head_dim, 3, 1, "elu1")
+        with torch.cuda.stream(s):
+            for c, o in zip(chunks, outs):
+                warm.step(*c, out=o, stream=s)
+        st = rh.StepState(1, wl.H, HW, wl.head_dim, 3, 1, "elu1")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c, o in zip(chunks, outs):
+                st.step(*c, out=o, stream=s)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        del g
+        rh.workspace_release(s)
+        return dt
+
+    dtg = stream_graph()
     return {"frames": frames, "ms_per_fwd": [round(m, 4) for m in ms],
             "slope_ms_per_21_frames": round(a * 21, 4), "intercept_ms": round(b, 4), "r2": round(r2, 5),
             "stream_105_frames": {"steps": 35, "ms": round(dt105 * 1000.0, 3),
                                   "vs_one_shot_105": round(dt105 * 1000.0 / ms[-1], 3),
+                                  "graph_ms": round(dtg * 1000.0, 3),
+                                  "graph_tokens_per_s": round(105 * HW / dtg, 1),
                                   "tokens_per_s": round(105 * HW / dt105, 1),
                                   "state_bytes": sb105, "state_bytes_at_21_frames": sb21,
                                   "extra_device_bytes_105": hw105, "extra_device_bytes_21": hw21}}

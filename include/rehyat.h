@@ -49,6 +49,12 @@
  *     Work queued on `stream` afterwards is ordered after the whole step, as
  *     for any other call, and graph capture of `stream` takes the side stream
  *     in.  rehyat_workspace_release() destroys that side stream too.
+ *   - Graph capture: the calls queue kernel launches and event records and
+ *     waits only (no memsets, copies or allocations), once the stream's
+ *     workspace (and, for streaming steps, its side stream) exists: make one
+ *     eager call on the stream before capturing it, or use
+ *     rehyat_attn_fwd_noalloc.  A captured stream of steps replays as that
+ *     stream from the state it started from.
  *   - Sizes: the rows of one (b, h) are addressed with 32-bit byte offsets, so
  *     frames * tokens_per_frame * (row bytes) must stay below 2^31, where a row
  *     is head_dim elements (2 head_dim with the learned maps); larger clips are

@@ -102,7 +102,8 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
     constexpr bool FEAT = PHI == kPhiFeat;            // phi(k) rows come precomputed
     constexpr int DP = PHI == kPhiElu1 ? D : 2 * D;
     constexpr int KW = FEAT ? DP : D;                 // columns of the K tile
-    constexpr int NW = state_nw(D, PHI), BN = kStateBN, NS = FEAT ? 3 : kStateStages;
+    constexpr int NW = state_nw(D, PHI), BN = kStateBN;
+    constexpr int NS = FEAT ? 3 : GRAD ? (kStateStages < 4 ? kStateStages : 4) : kStateStages;
     constexpr int NT = DP / 32;                       // 32-wide feature tiles
     constexpr int NTW = NT >= NW ? NT / NW : 1;       // feature tiles per wave
     constexpr int SPLIT = NT >= NW ? 1 : NW / NT;     // waves sharing a feature tile
@@ -117,7 +118,7 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
     static_assert(NT % NW == 0 || NW % NT == 0, "feature tiles must split evenly over the waves");
     static_assert(NLD % NW == 0, "tile loads must split evenly over the waves");
     static_assert(KSTEPS % SPLIT == 0, "16-key steps must split evenly over the waves sharing a tile");
-    static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
+    static_assert(NS >= 2 && NS <= 5, "2 to 5 LDS stages");
     static_assert(!GRAD || BN == 64, "one 4-byte-per-lane load carries a tile's lse (and one its dsum)");
 
     // the ring, reused at the end for the sums of the waves that share a feature tile
@@ -320,11 +321,14 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
         // every wave's have, and every wave is done with the slot refilled next
         const int ahead = min(NS - 2, ntiles - 1 - t);
         if (GRAD && grow_wave) {  // one more load per stage
-            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW + 2));
-            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW + 1));
+            constexpr int PER = OPW + 1;
+            if (ahead >= 3) __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * PER));
+            else if (ahead == 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * PER));
+            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(PER));
             else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         } else {
-            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
+            if (ahead >= 3) __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * OPW));
+            else if (ahead == 2) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * OPW));
             else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(OPW));
             else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         }
