@@ -527,19 +527,23 @@ def main():
                 "algorithmic_flops": cnt["softmax_flops"]}
     state = None
     if phi_dim > 0:
+        # The HBM fraction is taken with the last-level cache flushed before
+        # every step (512 MB written), so that K and V come from HBM; in the
+        # back-to-back steps of the main timing part of them is still in the
+        # cache (the warm_* figures, cache-assisted).
         st_ms = main_t["state_ms"] + main_t["scan_ms"]
-        gbs = cnt["state_bytes"] / (st_ms / 1000.0) / 1e9
-        state = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                 "frac": round(gbs / PEAK_HBM_GBS, 4), "state_kernel_ms": round(main_t["state_ms"], 4),
-                 "scan_ms": round(main_t["scan_ms"], 4), "algorithmic_bytes": cnt["state_bytes"]}
-        # the same with the last-level cache flushed before every step (512 MB written)
+        warm_gbs = cnt["state_bytes"] / (st_ms / 1000.0) / 1e9
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         ft = time_steps(rh, hip, qg, kg, vg, out, w, Tc, To, phi, max(5, args.steps // 2), 1, flush=scratch)
         del scratch
         fms = ft["state_ms"] + ft["scan_ms"]
-        state.update(flushed_state_kernel_ms=round(ft["state_ms"], 4), flushed_scan_ms=round(ft["scan_ms"], 4),
-                     flushed_achieved=round(cnt["state_bytes"] / (fms / 1000.0) / 1e9, 1),
-                     flushed_frac=round(cnt["state_bytes"] / (fms / 1000.0) / 1e9 / PEAK_HBM_GBS, 4))
+        gbs = cnt["state_bytes"] / (fms / 1000.0) / 1e9
+        state = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(gbs / PEAK_HBM_GBS, 4), "cache": "flushed before every step",
+                 "state_kernel_ms": round(ft["state_ms"], 4), "scan_ms": round(ft["scan_ms"], 4),
+                 "algorithmic_bytes": cnt["state_bytes"],
+                 "warm_state_kernel_ms": round(main_t["state_ms"], 4), "warm_scan_ms": round(main_t["scan_ms"], 4),
+                 "warm_achieved": round(warm_gbs, 1), "warm_frac": round(warm_gbs / PEAK_HBM_GBS, 4)}
 
     dense = None
     if not args.no_dense:
