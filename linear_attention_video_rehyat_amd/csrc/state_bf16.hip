@@ -121,8 +121,9 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
     static_assert(NS >= 2 && NS <= 5, "2 to 5 LDS stages");
     static_assert(!GRAD || BN == 64, "one 4-byte-per-lane load carries a tile's lse (and one its dsum)");
 
-    // the ring, reused at the end for the sums of the waves that share a feature tile
-    constexpr int RED_U16 = SPLIT > 1 ? 2 * ((SPLIT - 1) * NT * DT * 16 * 64 + (SPLIT - 1) * NT * 32) : 0;
+    // the ring, reused at the end for the sums of the waves that share a feature
+    // tile (one share at a time)
+    constexpr int RED_U16 = SPLIT > 1 ? 2 * (NT * DT * 16 * 64 + NT * 32) : 0;
     constexpr int SMEM_U16 = NS * STAGE > RED_U16 ? NS * STAGE : RED_U16;
     __shared__ __attribute__((aligned(16))) uint16_t smem_raw[SMEM_U16];
     lds_u16* const smem = (lds_u16*)smem_raw;
@@ -343,26 +344,30 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
 #pragma unroll
     for (int i = 0; i < NTW; ++i) z[i] = xhalf_sum(zpart[i]);
     if (SPLIT > 1) {
+        // shares 1, 2, ... added to share 0 in turn through one buffer
         __syncthreads();  // the ring is reused
-        float* red = (float*)smem_raw;  // [SPLIT-1][NT][DT][16][64] + z [SPLIT-1][NT][32]
-        float* zred = red + (SPLIT - 1) * NT * DT * 16 * 64;
-        if (kpart > 0) {
+        float* red = (float*)smem_raw;  // [NT][DT][16][64] + z [NT][32]
+        float* zred = red + NT * DT * 16 * 64;
+#pragma unroll 1
+        for (int sp = 1; sp < SPLIT; ++sp) {
+            if (kpart == sp) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) red[((((kpart - 1) * NT + nt0) * DT + dt) * 16 + r) * 64 + lane] = acc[0][dt][r];
-            if (lane < 32) zred[((kpart - 1) * NT + nt0) * 32 + lq] = z[0];
+                    for (int r = 0; r < 16; ++r) red[((nt0 * DT + dt) * 16 + r) * 64 + lane] = acc[0][dt][r];
+                if (lane < 32) zred[nt0 * 32 + lq] = z[0];
+            }
+            __syncthreads();
+            if (kpart == 0) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[0][dt][r] += red[((nt0 * DT + dt) * 16 + r) * 64 + lane];
+                z[0] += lane < 32 ? zred[nt0 * 32 + lq] : 0.0f;
+            }
+            __syncthreads();
         }
-        __syncthreads();
         if (kpart > 0) return;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-#pragma unroll
-                for (int sp = 1; sp < SPLIT; ++sp) acc[0][dt][r] += red[((((sp - 1) * NT + nt0) * DT + dt) * 16 + r) * 64 + lane];
-#pragma unroll
-        for (int sp = 1; sp < SPLIT; ++sp) z[0] += lane < 32 ? zred[((sp - 1) * NT + nt0) * 32 + lq] : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
