@@ -1137,6 +1137,20 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
     // most one workgroup per CU that launch leaves idle, each taking several
     // sub-blocks in turn: a workgroup sent to a shader engine with no idle CU
     // would wait for the local launch to end.
+    // the copy of the last min(T_o, frames so far) frames for the next window
+    // (into the other K/V slot: this step's launches read this one)
+    PrevCopyParams pc{};
+    if (copy) {
+        pc.kp = lp.kp; pc.vp = lp.vp; pc.prev_bh_stride = lp.prev_bh_stride; pc.prev_rows = P;
+        pc.k = k; pc.v = v; pc.bh_stride = n * g.d; pc.chunk_rows = (int)n;
+        pc.kd = base + L.kp_off[cur ^ 1]; pc.vd = base + L.vp_off[cur ^ 1];
+        pc.keep_rows = keep_rows; pc.BH = g.BH; pc.d = g.d; pc.elem_bytes = g.elem;
+        if (mlp) {
+            pc.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; pc.fk = base + L.fk_off; pc.fkd = base + L.fkp_off[cur ^ 1];
+            pc.fprev_bh_stride = (long long)g.To * g.HW * g.Dp; pc.f_bh_stride = n * g.Dp; pc.f_cols = g.Dp;
+        }
+    }
+    bool copied = false;  // done by the fold's workgroups
     StateParams sp{};
     if (fold) {
         sp.k = k; sp.v = v; sp.kp = lp.kp; sp.vp = lp.vp;
@@ -1156,6 +1170,12 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
         const int idle = cus_per_xcd() * 8 - lp.tiles_per_chunk * lp.BH;
         const int items = sp.items_per_bh * g.BH;
         if (idle > 0 && items > idle) sp.wg_items = (items + idle - 1) / idle;
+        // those few workgroups finish long before the local launch: they also
+        // make the copy (bf16 K and V; the learned map's phi(K) plane stays below)
+        if (copy && !mlp && g.dtype == REHYAT_BF16 && sp.wg_items > 1) {
+            sp.copy = pc;
+            copied = true;
+        }
         e = hip_step([&] { return g.dtype == REHYAT_BF16 ? launch_state_bf16(sp, a) : launch_state_f32(sp, a); });
         if (e != hipSuccess) return failed(e, "block-state launch");
         e = hip_step([&] { return hipEventRecord(side.side->join, a); });
@@ -1167,10 +1187,9 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
         }
         forked = false;
     }
-    // 3. after the local launch (which reads the prepared state and the K/V
-    // slot), on the caller's stream, in one launch: add the fold into (S, z)
-    // and prepare it for the next step; keep the last min(T_o, frames so far)
-    // frames for the next window in the other K/V slot
+    // 3. after the local launch (which reads the prepared state), on the
+    // caller's stream, in one launch: add the fold into (S, z) and prepare it
+    // for the next step, and the overlap copy unless the fold made it
     bool nonempty = st->state_nonempty != 0;
     ScanParams cp{};
     if (fold) {
@@ -1185,19 +1204,9 @@ static rehyat_status step_impl(rehyat_step_state* st, const void* q, const void*
         cp.mode = kCausal; cp.C = 1; cp.q = 0; cp.suffix = nullptr;
         nonempty = true;
     }
-    PrevCopyParams pc{};
-    if (copy) {
-        pc.kp = lp.kp; pc.vp = lp.vp; pc.prev_bh_stride = lp.prev_bh_stride; pc.prev_rows = P;
-        pc.k = k; pc.v = v; pc.bh_stride = n * g.d; pc.chunk_rows = (int)n;
-        pc.kd = base + L.kp_off[cur ^ 1]; pc.vd = base + L.vp_off[cur ^ 1];
-        pc.keep_rows = keep_rows; pc.BH = g.BH; pc.d = g.d; pc.elem_bytes = g.elem;
-        if (mlp) {
-            pc.fkp = P > 0 ? base + L.fkp_off[cur] : nullptr; pc.fk = base + L.fk_off; pc.fkd = base + L.fkp_off[cur ^ 1];
-            pc.fprev_bh_stride = (long long)g.To * g.HW * g.Dp; pc.f_bh_stride = n * g.Dp; pc.f_cols = g.Dp;
-        }
-    }
-    if (fold || copy) {
-        e = hip_step([&] { return launch_scan_copy(fold ? &cp : nullptr, copy ? &pc : nullptr, s); });
+    const bool copy_here = copy && !copied;
+    if (fold || copy_here) {
+        e = hip_step([&] { return launch_scan_copy(fold ? &cp : nullptr, copy_here ? &pc : nullptr, s); });
         if (e != hipSuccess) return hip_fail(e, "state update launch");
     }
     st->prev_slot = copy ? cur ^ 1 : cur;

@@ -152,6 +152,18 @@ __host__ __device__ inline int local_work_item(const LocalParams& p, int bid, in
     }
 }
 
+// Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot
+// (K, V and, for the learned map, phi(K) rows of f_cols columns).
+struct PrevCopyParams {
+    const void* kp; const void* vp; long long prev_bh_stride; int prev_rows;
+    const void* k; const void* v; long long bh_stride; int chunk_rows;
+    void* kd; void* vd;               // destination slot, same stride as prev
+    int keep_rows, BH, d, elem_bytes;
+    const void* fkp; const void* fk; void* fkd;   // phi(K) rows or null
+    long long fprev_bh_stride, f_bh_stride;
+    int f_cols;
+};
+
 // Block-state pass: partial S^T = sum phi(k) v^T (stored [d][D'] fp32) and
 // z = sum phi(k) over contiguous key sub-blocks of each delta block E_u.
 struct StateParams {
@@ -178,6 +190,9 @@ struct StateParams {
     // bf16 elu+1 / poly2: sub-blocks per workgroup (0 or 1: one workgroup each);
     // more: fewer workgroups take the sub-blocks in turn (same results)
     int wg_items;
+    // with wg_items > 1 (the streaming fold): the overlap copy of the step,
+    // done by the same workgroups after their sub-blocks (keep_rows 0: none)
+    PrevCopyParams copy;
 };
 
 // The blocks of a state partition and their sub-blocks: block u covers rows
@@ -254,18 +269,6 @@ struct BwdParams {
     int mode;                         // kCausal or kBidirectional (then: G per bidirectional block,
                                       // 2C+1 slots, and every chunk has a linear set)
     int dq_lpt;                       // dq workgroups: each XCD's items longest first (local_work_item)
-};
-
-// Copy of the last `keep_rows` rows of [prev | chunk] into the other overlap slot
-// (K, V and, for the learned map, phi(K) rows of f_cols columns).
-struct PrevCopyParams {
-    const void* kp; const void* vp; long long prev_bh_stride; int prev_rows;
-    const void* k; const void* v; long long bh_stride; int chunk_rows;
-    void* kd; void* vd;               // destination slot, same stride as prev
-    int keep_rows, BH, d, elem_bytes;
-    const void* fkp; const void* fk; void* fkd;   // phi(K) rows or null
-    long long fprev_bh_stride, f_bh_stride;
-    int f_cols;
 };
 
 // Learned feature map (ReHyAt §3.2 polynomial form with a two-layer MLP, §4.3 /

@@ -11,6 +11,7 @@
 // chunks included) the state of chunk t is a prefix plus a suffix of the block
 // sums, kept as two separate sums rather than a total minus the window.
 #include "common.h"
+#include "copy_rows.h"
 #include "kernels.h"
 
 namespace rehyat {
@@ -222,28 +223,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
     const int e4 = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (e4 >= p.d * p.Dp + p.Dp) return;
     scan_elem(p, blockIdx.y, e4);
-}
-
-// 16-byte chunk idx of the kept rows (chunks of a row: d * elem_bytes / 16).
-__device__ __forceinline__ void prev_copy_chunk(const PrevCopyParams& p, const int cpr, const long long idx) {
-    const int c = (int)(idx % cpr);
-    const long long rr = idx / cpr;
-    const int r = (int)(rr % p.keep_rows);
-    const int bh = (int)(rr / p.keep_rows);
-    const int j = p.prev_rows + p.chunk_rows - p.keep_rows + r;   // virtual row of [prev | chunk]
-    const char* ks;
-    const char* vs;
-    const long long rowb = (long long)p.d * p.elem_bytes;
-    if (j < p.prev_rows) {
-        ks = (const char*)p.kp + ((long long)bh * p.prev_bh_stride) * p.elem_bytes + j * rowb;
-        vs = (const char*)p.vp + ((long long)bh * p.prev_bh_stride) * p.elem_bytes + j * rowb;
-    } else {
-        ks = (const char*)p.k + ((long long)bh * p.bh_stride) * p.elem_bytes + (j - p.prev_rows) * rowb;
-        vs = (const char*)p.v + ((long long)bh * p.bh_stride) * p.elem_bytes + (j - p.prev_rows) * rowb;
-    }
-    const long long doff = ((long long)bh * p.prev_bh_stride) * p.elem_bytes + r * rowb + 16LL * c;
-    *(u32x4*)((char*)p.kd + doff) = *(const u32x4*)(ks + 16LL * c);
-    if (p.vd) *(u32x4*)((char*)p.vd + doff) = *(const u32x4*)(vs + 16LL * c);
 }
 
 __global__ __launch_bounds__(256) void prev_copy_kernel(PrevCopyParams p) {

@@ -24,6 +24,7 @@
 // transposing reads are the B fragments as they are, one MFMA per output tile.
 #include <type_traits>
 
+#include "copy_rows.h"
 #include "local_common.h"
 
 namespace rehyat {
@@ -400,6 +401,15 @@ __global__ __launch_bounds__(state_nw(D, PHI) * 64) void state_bf16_multi_kernel
     for (int item = blockIdx.x; item < n; item += gridDim.x) {
         state_item<D, PHI, false>(p, item);
         __syncthreads();  // the next item refills the ring
+    }
+    // then the step's overlap copy (these workgroups finish well before the
+    // local launch they run beside)
+    if (p.copy.keep_rows > 0) {
+        const int cpr = p.copy.d * p.copy.elem_bytes / 16;
+        const long long total = (long long)p.copy.BH * p.copy.keep_rows * cpr;
+        const int nt = state_nw(D, PHI) * 64;
+        for (long long idx = (long long)blockIdx.x * nt + threadIdx.x; idx < total; idx += (long long)gridDim.x * nt)
+            prev_copy_chunk(p.copy, cpr, idx);
     }
 }
 

@@ -167,3 +167,18 @@ def test_streams_on_two_user_streams_interleaved():
     for j in (0, 1):
         assert torch.equal(torch.cat(outs[j], dim=2), refs[j]), j
     rh.workspace_release(streams[1])
+
+
+@pytest.mark.parametrize("phi", ["elu1", "poly2"])
+def test_stream_fold_beside_a_nearly_full_local_launch(phi):
+    """31 heads of 2048-token frames, one frame per step: each local launch has
+    8 x 31 = 248 workgroups, so on 256 CUs the fold (62 sub-blocks) runs with a
+    capped grid, its workgroups taking sub-blocks in turn and then making the
+    overlap copy; the stream still equals the whole-clip forward bit for bit."""
+    B, H, F, HW, d, Tc, To = 1, 31, 6, 2048, 128, 1, 1
+    w = inputs.custom(B, H, F, HW, d, Tc, To, dtype="bf16", seed_id=540)
+    q, k, v = gpu(*inputs.make_qkv(w))
+    y_fwd = rh.attn_fwd(q, k, v, F, HW, Tc, To, phi)
+    y_st, _ = _stream(q, k, v, HW, Tc, To, phi)
+    sync()
+    assert torch.equal(y_st, y_fwd)
