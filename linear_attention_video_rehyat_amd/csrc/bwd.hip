@@ -270,9 +270,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
                             u32x4 whi, wlo;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float h0 = round_bf16(f[2 * e]), h1 = round_bf16(f[2 * e + 1]);
-                                whi[e] = pack2_bf16(h0, h1);
-                                wlo[e] = pack2_bf16(f[2 * e] - h0, f[2 * e + 1] - h1);
+                                const u32x2 hl = split2_bf16(f[2 * e], f[2 * e + 1]);
+                                whi[e] = hl[0];
+                                wlo[e] = hl[1];
                             }
                             const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
                             const bf16x8 ah = __builtin_bit_cast(bf16x8, ldg_b128(ghi + off));

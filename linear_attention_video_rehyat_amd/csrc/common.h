@@ -44,6 +44,19 @@ __device__ __forceinline__ float round_bf16(float a) {
     return (float)(__bf16)a;
 }
 
+// Two-term bf16 split of a pair, returned as {hi, lo}: hi = the pair rounded to
+// bf16 (nearest-even, low element first), lo = the bf16 rounding of a - hi_a and
+// b - hi_b, so that hi + lo carries about 16 significant bits.  One conversion
+// yields both hi halves, which widen back to fp32 exactly by shifting and masking
+// (the empty asm keeps the compiler from converting the low element again for
+// the shift).
+__device__ __forceinline__ u32x2 split2_bf16(float a, float b) {
+    uint32_t hi = pack2_bf16(a, b);
+    asm("" : "+v"(hi));
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+    return u32x2{hi, pack2_bf16(a - ha, b - hb)};
+}
+
 // elu(x) + 1 with alpha = 1.
 __device__ __forceinline__ float elu1(float x) {
     return x > 0.0f ? x + 1.0f : __expf(x);

@@ -103,9 +103,9 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
         u32x4 whi, wlo;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float h0 = round_bf16(f[2 * j]), h1 = round_bf16(f[2 * j + 1]);
-            whi[j] = pack2_bf16(h0, h1);
-            wlo[j] = pack2_bf16(f[2 * j] - h0, f[2 * j + 1] - h1);
+            const u32x2 hl = split2_bf16(f[2 * j], f[2 * j + 1]);
+            whi[j] = hl[0];
+            wlo[j] = hl[1];
         }
         fh = __builtin_bit_cast(bf16x8, whi);
         fl = __builtin_bit_cast(bf16x8, wlo);

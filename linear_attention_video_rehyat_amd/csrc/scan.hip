@@ -38,10 +38,9 @@ __device__ __forceinline__ void scan_elem(const ScanParams& p, const int bh, con
                 uint32_t hi[2], lo[2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const float a = x[2 * j], b = x[2 * j + 1];
-                    const float ha = round_bf16(a), hb = round_bf16(b);
-                    hi[j] = pack2_bf16(ha, hb);
-                    lo[j] = pack2_bf16(a - ha, b - hb);
+                    const u32x2 hl = split2_bf16(x[2 * j], x[2 * j + 1]);
+                    hi[j] = hl[0];
+                    lo[j] = hl[1];
                 }
                 *(u32x2*)((uint16_t*)p.s_hi + off) = u32x2{hi[0], hi[1]};
                 *(u32x2*)((uint16_t*)p.s_lo + off) = u32x2{lo[0], lo[1]};

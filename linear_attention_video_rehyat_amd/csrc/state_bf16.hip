@@ -296,16 +296,18 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
                 u32x4 whi, wlo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float h0 = round_bf16(f[2 * e]), h1 = round_bf16(f[2 * e + 1]);
-                    whi[e] = pack2_bf16(h0, h1);
-                    wlo[e] = pack2_bf16(f[2 * e] - h0, f[2 * e + 1] - h1);
+                    const u32x2 hl = split2_bf16(f[2 * e], f[2 * e + 1]);
+                    whi[e] = hl[0];
+                    wlo[e] = hl[1];
                 }
                 const bf16x8 bhi = __builtin_bit_cast(bf16x8, whi), blo = __builtin_bit_cast(bf16x8, wlo);
+                // every hi product, then every lo product: consecutive products go to
+                // different accumulators, so none waits for the one before it (each
+                // accumulator still adds hi, then lo)
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    acc[i][dt] = mfma32x32x16(a[dt], bhi, acc[i][dt]);
-                    acc[i][dt] = mfma32x32x16(a[dt], blo, acc[i][dt]);
-                }
+                for (int dt = 0; dt < DT; ++dt) acc[i][dt] = mfma32x32x16(a[dt], bhi, acc[i][dt]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[i][dt] = mfma32x32x16(a[dt], blo, acc[i][dt]);
             }
         }
     };
