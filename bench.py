@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "ccf713e86574e8a3", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (251972.4 * 2.0 + 98280.5 * 1.0) * 1024}
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "114ef1ec0d10f086", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (251785.4 * 2.0 + 98282.7 * 1.0) * 1024}
 
 
 LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h")
@@ -504,6 +504,10 @@ def main():
     import linear_attention_video_rehyat_amd as rh
     from linear_attention_video_rehyat_amd import inputs
 
+    def progress(part):
+        # one line per finished part on stderr (stdout carries only the JSON line)
+        print(f"bench.py: {part} done", file=sys.stderr, flush=True)
+
     w = inputs.WORKLOADS[args.workload]
     Tc = args.chunk_frames or w.chunk_frames
     To = w.overlap_frames
@@ -517,6 +521,7 @@ def main():
     torch.cuda.synchronize()
 
     main_t = time_steps(rh, hip, qg, kg, vg, out, w, Tc, To, phi, args.steps, args.warmup)
+    progress("main timing")
     cnt = geometry_counts(w, Tc, To, phi_dim)
     value = w.tokens / (main_t["ms_per_step"] / 1000.0)
     local_tflops = cnt["softmax_flops"] / (main_t["local_ms"] / 1000.0) / 1e12
@@ -544,6 +549,7 @@ def main():
                  "algorithmic_bytes": cnt["state_bytes"],
                  "warm_state_kernel_ms": round(main_t["state_ms"], 4), "warm_scan_ms": round(main_t["scan_ms"], 4),
                  "warm_achieved": round(warm_gbs, 1), "warm_frac": round(warm_gbs / PEAK_HBM_GBS, 4)}
+        progress("state pass (flushed)")
 
     dense = None
     if not args.no_dense:
@@ -554,6 +560,7 @@ def main():
                  "tflops": round(dc["softmax_flops"] / (d_t["local_ms"] / 1000.0) / 1e12, 2),
                  "hybrid_speedup": round(d_t["ms_per_step"] / main_t["ms_per_step"], 3),
                  "flop_ratio": round(dc["softmax_flops"] / cnt["softmax_flops"], 3)}
+        progress("dense softmax")
 
     bidir = None
     if not args.no_bidir:
@@ -569,23 +576,28 @@ def main():
                          state_pass_frac=round(cnt["bidir_state_bytes"] / (bst / 1000.0) / 1e9
                                                / PEAK_HBM_GBS, 4),
                          state_algorithmic_bytes=cnt["bidir_state_bytes"])
+        progress("bidirectional")
 
     learned = None
     if not args.no_learned:
         learned = learned_map_bench(rh, hip, inputs, qg, kg, vg, out, w, Tc, To, args.learned_hidden,
                                     max(3, args.steps // 2), cnt)
+        progress("learned maps")
 
     backward = None
     if not args.no_backward and phi in ("elu1", "poly2", "none"):
         backward = backward_bench(rh, inputs, qg, kg, vg, w, Tc, To, phi, max(3, args.steps // 2), cnt)
+        progress("backward")
 
     sweep = None
     if not args.no_sweep and w.name == "wan_21x30x52" and phi == "elu1":
         sweep = workload_sweep(rh, hip, inputs, max(3, args.steps // 4))
+        progress("other workloads")
 
     length = None
     if not args.no_length and w.name == "wan_21x30x52" and Tc == 3 and phi == "elu1":
         length = length_scaling_bench(rh, hip, inputs, min(args.warmup, 5))
+        progress("length scaling")
 
     blocks = None
     if not args.no_blocks and w.name == "wan_21x30x52" and phi in ("elu1", "poly2"):
@@ -593,10 +605,12 @@ def main():
         if dense is not None:
             dense_attn = dense["ms_per_step"]
         blocks = block_bench(rh, inputs, w, Tc, To, phi, max(3, args.steps // 4), main_t["ms_per_step"], dense_attn)
+        progress("attention blocks")
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, Tc, To, phi, args.cpu_seconds)
+        progress("cpu baseline")
 
     line = {
         "metric": "hybrid-attn fwd tokens/s at Wan2.1-1.3B shape; % of MFMA/HBM roofline",
