@@ -156,35 +156,62 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
     const float invl = 1.0f / lsum;
     const float invn = nl > 0.0f ? 1.0f / nl : 0.0f;
     uint16_t* ob_ptr = (uint16_t*)p.out + bh * p.bh_stride;
-    // one 32-column slice of the output at a time: a^L^T = S_t^T phi(Q)^T with a
-    // three-pass bf16 split (hi*hi + lo*hi + hi*lo) of both operands
+    // a^L^T = S_t^T phi(Q)^T with a three-pass bf16 split (hi*hi + lo*hi + hi*lo)
+    // of both operands.  Fragment (32-column slice dt, 16-feature step ksl) of
+    // the staged copies in LDS (DP / 8 chunks per row, by issue_state_dma) or
+    // of the prepared state in global memory:
+    auto state_frag = [&](int dt, int ksl, bf16x8& ahi, bf16x8& alo) {
+        if (s_lds) {
+            const int off = (32 * dt + lq) * DP + (((2 * ksl + h) ^ swz<DP / 8>(lq)) << 3);
+            ahi = lds_read_b128(s_lds, off);
+            alo = lds_read_b128(s_lds_lo, off);
+        } else {
+            const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
+            ahi = __builtin_bit_cast(bf16x8, ldg_b128(shi + off));
+            alo = __builtin_bit_cast(bf16x8, ldg_b128(slo + off));
+        }
+    };
+    // Without the phi(q) fragments in registers, each 16-feature step's phi is
+    // formed once for all four slices, whose accumulators then interleave (each
+    // slice still adds its products in the same order).  With them, one slice
+    // at a time: the four accumulators at once cost the main loop more than the
+    // chains' latency does (measured 1.2 % slower at d = 128).
+    f32x16 lall[KEEP ? 1 : DT];
+    if constexpr (!KEEP) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        f32x16 lacc = f32x16{};
+        for (int dt = 0; dt < DT; ++dt) lall[dt] = f32x16{};
         if (lin) {
 #pragma unroll
             for (int ksl = 0; ksl < KSL; ++ksl) {
-                bf16x8 ahi, alo;
-                if (s_lds) {  // copies staged in LDS by issue_state_dma (DP / 8 chunks per row)
-                    const int off = (32 * dt + lq) * DP + (((2 * ksl + h) ^ swz<DP / 8>(lq)) << 3);
-                    ahi = lds_read_b128(s_lds, off);
-                    alo = lds_read_b128(s_lds_lo, off);
-                } else {
-                    const long long off = (long long)(32 * dt + lq) * DP + 16 * ksl + 8 * h;
-                    ahi = __builtin_bit_cast(bf16x8, ldg_b128(shi + off));
-                    alo = __builtin_bit_cast(bf16x8, ldg_b128(slo + off));
-                }
                 bf16x8 fh, fl;
-                if (KEEP) {
-                    fh = fhi[KEEP ? ksl : 0];
-                    fl = FEAT ? bf16x8{} : flo[KEEP && !FEAT ? ksl : 0];
-                } else {
-                    float f[8];
-                    phi_frag(ksl, fh, fl, f);
-                }
+                float f[8];
+                phi_frag(ksl, fh, fl, f);
+                bf16x8 ahi[DT], alo[DT];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) state_frag(dt, ksl, ahi[dt], alo[dt]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) lall[dt] = mfma32x32x16(ahi[dt], fh, lall[dt]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) lall[dt] = mfma32x32x16(alo[dt], fh, lall[dt]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) lall[dt] = mfma32x32x16(ahi[dt], fl, lall[dt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        f32x16 lacc = f32x16{};
+        if constexpr (!KEEP) {
+            lacc = lall[dt];
+        } else if (lin) {
+#pragma unroll
+            for (int ksl = 0; ksl < KSL; ++ksl) {
+                bf16x8 ahi, alo;
+                state_frag(dt, ksl, ahi, alo);
+                const bf16x8 fh = fhi[ksl];
                 lacc = mfma32x32x16(ahi, fh, lacc);
                 lacc = mfma32x32x16(alo, fh, lacc);
-                if (!FEAT) lacc = mfma32x32x16(ahi, fl, lacc);
+                if (!FEAT) lacc = mfma32x32x16(ahi, flo[FEAT ? 0 : ksl], lacc);
             }
         }
         if (!valid) continue;
