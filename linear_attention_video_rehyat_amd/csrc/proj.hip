@@ -14,15 +14,17 @@
 // 128-token tile of the transposed product C^T = W X^T on
 // v_mfma_f32_32x32x16_bf16 (A = W rows, B = X rows: both operands are rows
 // with the reduction dimension contiguous, so every fragment is one 16-byte
-// LDS read); each wave owns 64 features x 64 tokens (2 x 2 MFMA tiles).  W and
-// X tiles of 32 input features stream through a 4-stage LDS ring by direct
-// global->LDS loads (three tiles in flight), rows XOR-swizzled.  In the C
+// LDS read).  The large tiles: 256 features x 256 tokens, 8 waves of 128 x 64
+// (4 x 2 MFMA tiles), W and X tiles of 64 input features double-buffered in
+// LDS; the small ones (any width that is a multiple of 128): 128 x 128, 4 waves
+// of 64 x 64, tiles of 32 input features in a 4-stage ring.  Tiles arrive by
+// direct global->LDS loads, rows XOR-swizzled.  In the C
 // layout a lane holds one token and, per group of four registers, four
 // consecutive features, so the epilogue stores 8 bytes at a time:
 //   QKV: + bias, k scaled by 1/sqrt(d), bf16, scattered to q, k, v in the
 //        [B][H][N][d] layout the attention takes;
 //   OUT: X rows are gathered from the attention output's [B][H][N][d] layout
-//        (a 32-feature k-tile lies within one head), + bias + the residual x,
+//        (a k-tile lies within one head), + bias + the residual x,
 //        bf16, token-major [B*N][C].
 #include "local_common.h"
 
@@ -30,16 +32,19 @@ namespace rehyat {
 
 namespace {
 
-constexpr int kProjBK = 32;    // input features per LDS stage
+constexpr int kProjMinBK = 32;  // input features per LDS stage, at least
 constexpr int kProjMinBF = 128;
 
 // Tile configurations: workgroup tile BF features x BT tokens, NW waves in a
 // WGF x (NW / WGF) grid, each wave (BF / WGF) features x (BT * WGF / NW)
-// tokens, NS LDS stages.
+// tokens, NS LDS stages of BK input features.  Measured at the Wan shape (QKV
+// projection, one process): 256 x 256 with 3 stages of 32 features 550 us,
+// with 4 stages 551 us, with 2 stages of 64 features 513 us; 4 waves of 128 x
+// 128 (accumulators in AGPRs, one wave per SIMD) 679 us.
 struct ProjCfg {
-    int BF, BT, NW, WGF, NS;
+    int BF, BT, NW, WGF, NS, BK;
 };
-constexpr ProjCfg kProjCfgs[3] = {{128, 128, 4, 2, 4}, {256, 256, 8, 2, 3}, {256, 128, 8, 4, 4}};
+constexpr ProjCfg kProjCfgs[3] = {{128, 128, 4, 2, 4, 32}, {256, 256, 8, 2, 2, 64}, {256, 128, 8, 4, 4, 32}};
 #ifndef REHYAT_PROJ_CFG
 #define REHYAT_PROJ_CFG 1
 #endif
@@ -51,7 +56,7 @@ template <int MODE, int CFG>
 __device__ __forceinline__ void proj_body(const ProjParams& p) {
     constexpr int BF = kProjCfgs[CFG].BF, BT = kProjCfgs[CFG].BT, NW = kProjCfgs[CFG].NW;
     constexpr int WGF = kProjCfgs[CFG].WGF, NS = kProjCfgs[CFG].NS;
-    constexpr int BK = kProjBK;
+    constexpr int BK = kProjCfgs[CFG].BK;
     constexpr int WGT = NW / WGF;
     constexpr int MI = BF / WGF / 32, NJ = BT / WGT / 32;  // 32x32 MFMA tiles per wave
     constexpr int CK = BK / 8;                       // 16-byte chunks per tile row
@@ -220,13 +225,15 @@ __global__ __launch_bounds__(64 * 8) void proj_bf16_kernel(ProjParams p) {
 }  // namespace
 
 bool proj_shape_ok(int c_in, int n_out, int head_dim) {
-    return c_in % kProjBK == 0 && n_out % kProjMinBF == 0 && head_dim % kProjBK == 0 && c_in % head_dim == 0;
+    return c_in % kProjMinBK == 0 && n_out % kProjMinBF == 0 && head_dim % kProjMinBK == 0 && c_in % head_dim == 0;
 }
 
 hipError_t launch_proj_bf16(const ProjParams& p, hipStream_t s) {
-    // the larger tiles where the features split into them, else 128 x 128
+    // the larger tiles where the features and the input width split into them
+    // (OUT gathers its input by heads: a k-tile must lie within one head), else
+    // 128 x 128
     const ProjCfg c = kProjCfgs[REHYAT_PROJ_CFG];
-    const bool big = REHYAT_PROJ_CFG != 0 && p.n_out % c.BF == 0;
+    const bool big = REHYAT_PROJ_CFG != 0 && p.n_out % c.BF == 0 && p.c_in % c.BK == 0 && p.d % c.BK == 0;
     const ProjCfg u = big ? c : kProjCfgs[0];
     const long long tiles = (long long)(p.n_out / u.BF) * ((p.T + u.BT - 1) / u.BT);
     if (tiles <= 0) return hipSuccess;
