@@ -37,7 +37,9 @@ def _check(out, x, ref_a, rows=None, what=""):
     return r, a
 
 
-SMALL = [(1, 2, 128, 5, 40, 2, 1), (2, 4, 64, 4, 37, 1, 1), (1, 12, 128, 3, 50, 3, 1)]
+# the last geometry (width 128, head_dim 32) takes the projections' 128 x 128 tiles
+# with 32-feature LDS stages; the others the 256 x 256 tiles with 64-feature stages
+SMALL = [(1, 2, 128, 5, 40, 2, 1), (2, 4, 64, 4, 37, 1, 1), (1, 12, 128, 3, 50, 3, 1), (1, 4, 32, 3, 20, 1, 1)]
 
 
 @pytest.mark.parametrize("geom", SMALL, ids=lambda g: "B{}H{}d{}F{}HW{}Tc{}To{}".format(*g))
