@@ -477,6 +477,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-blocks", action="store_true")
+    ap.add_argument("--no-combine", action="store_true")
     ap.add_argument("--learned-hidden", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -551,6 +552,28 @@ def main():
                  "warm_achieved": round(warm_gbs, 1), "warm_frac": round(warm_gbs / PEAK_HBM_GBS, 4)}
         progress("state pass (flushed)")
 
+    combine = None
+    if not args.no_combine and phi_dim > 0:
+        # The linear query branch and the joint normalisation run fused in the
+        # local kernel's epilogue; their cost is the local kernel's time with
+        # the feature map on, less its time with it off (phi = NONE: the same
+        # windows and tiles, softmax-only epilogue).  Linear FLOPs per query of
+        # a chunk with a linear set: a^L = phi(q)^T S_t (2 D' d) and
+        # n^L = phi(q).z_t (2 D').
+        n_t = time_steps(rh, hip, qg, kg, vg, out, w, Tc, To, "none", max(5, args.steps // 2), 5)
+        hybrid_t = time_steps(rh, hip, qg, kg, vg, out, w, Tc, To, phi, max(5, args.steps // 2), 5)
+        lin_q = sum(max(min((t + 1) * Tc, w.frames) - t * Tc, 0) for t in range(1, cnt["chunks"])
+                    if t * Tc - To > 0) * w.tokens_per_frame * w.B * w.H
+        marginal = hybrid_t["local_ms"] - n_t["local_ms"]
+        combine = {"local_ms_softmax_only": round(n_t["local_ms"], 4),
+                   "local_ms_with_linear_branch": round(hybrid_t["local_ms"], 4),
+                   "marginal_ms": round(marginal, 4),
+                   "marginal_share_of_local": round(marginal / hybrid_t["local_ms"], 4),
+                   "linear_queries": lin_q,
+                   "linear_gflop": round(lin_q * (2.0 * phi_dim * w.head_dim + 2.0 * phi_dim) / 1e9, 2),
+                   "out_bytes": w.B * w.H * w.frames * w.tokens_per_frame * w.head_dim * 2}
+        progress("fused combine")
+
     dense = None
     if not args.no_dense:
         d_t = time_steps(rh, hip, qg, kg, vg, out, w, w.frames, 0, "none", max(3, args.steps // 4), 1)
@@ -624,6 +647,7 @@ def main():
                    "tokens_per_step": w.tokens},
         "roofline": roofline,
         "state_pass": state,
+        "combine": combine,
         "dense_softmax": dense,
         "bidirectional": bidir,
         "learned_map": learned,
