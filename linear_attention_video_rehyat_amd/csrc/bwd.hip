@@ -349,6 +349,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
         const int st = t % NST;
         const lds_u16* Qs = (const lds_u16*)tiles_raw[st];
         const lds_u16* Ys = Qs + QT;
+        asm volatile("" : "+v"(Ys));  // the two tiles' reads keep bases of their own
         // the subtiles' S^T chains side by side (independent accumulators)
         f32x16 sall[NQS];
 #pragma unroll
@@ -423,6 +424,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
         const int st = t % NST;
         const lds_u16* Qs = (const lds_u16*)tiles_raw[st];
         const lds_u16* Ys = Qs + QT;
+        asm volatile("" : "+v"(Ys));  // the two tiles' reads keep bases of their own
         f32x16 pall[NQS];
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs) pall[qs] = f32x16{};
@@ -473,8 +475,11 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
         }
     }
     // iteration it: the first waves take tile it, the second waves tile it - 1;
-    // the ring holds tiles it - 1, it and (being loaded) it + 1
-    for (int it = 0; it <= ntiles && ntiles > 0; ++it) {
+    // the ring holds tiles it - 1, it and (being loaded) it + 1.  Each role has
+    // a loop of its own (the same barriers, one per iteration): in one loop
+    // shared by both, the accumulators of the two roles' paths were given
+    // different registers and copied over (32 64-bit moves) every iteration.
+    auto iteration_start = [&](int it) {
         // own loads of tile it and own LDS writes (P, row data) have landed,
         // then every wave's have
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
@@ -484,7 +489,11 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
             load_tile((it + 1) % NST, it + 1);
             if (wave < RW) fetch_rows(it + 1);
         }
-        if (first) {
+        return more;
+    };
+    if (first) {
+        for (int it = 0; it <= ntiles && ntiles > 0; ++it) {
+            const bool more = iteration_start(it);
             if (it < ntiles) {
                 // windows move forward with the row: the tile needs no mask when
                 // its first row's window ends after the block and its last row's
@@ -498,10 +507,14 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
                 else
                     first_step(it, std::false_type{});
             }
-        } else {
-            if (it > 0) second_step(it - 1);
+            if (more && wave < RW) store_rows((it + 1) % NST);
         }
-        if (more && wave < RW) store_rows((it + 1) % NST);
+    } else {
+        for (int it = 0; it <= ntiles && ntiles > 0; ++it) {
+            const bool more = iteration_start(it);
+            if (it > 0) second_step(it - 1);
+            if (more && wave < RW) store_rows((it + 1) % NST);
+        }
     }
 
     if (!key_ok) return;

@@ -313,14 +313,17 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
     };
     // the slot being filled and the slot being read never overlap; as restrict
     // pointers they keep the transposing reads clear of a wait for the loads
-    auto iteration = [&](int t, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
+    auto iteration = [&](auto tail, int t, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
         if (t + NS - 1 < ntiles) load_tile(fill, t + NS - 1);
-        if ((t + 1) * BN <= nkeys) tile_steps(std::false_type{}, t, cur, cur + KTILE);
-        else tile_steps(std::true_type{}, t, cur, cur + KTILE);
+        tile_steps(tail, t, cur, cur + KTILE);
     };
 
     for (int t = 0; t < NS - 1 && t < ntiles; ++t) load_tile(smem + t * STAGE, t);
-    for (int t = 0; t < ntiles; ++t) {
+    // the last tile, the only one that can be partial, is peeled off the loop
+    // and alone masks keys past the sub-block: with both forms inside the
+    // loop, the two paths left the accumulators in different registers and
+    // every iteration copied them back (32 64-bit moves per tile and wave)
+    auto step = [&](auto tail, int t) {
         // own loads of tile t have landed (later tiles may be in flight), then
         // every wave's have, and every wave is done with the slot refilled next
         const int ahead = min(NS - 2, ntiles - 1 - t);
@@ -337,8 +340,10 @@ __device__ __forceinline__ void state_item(const StateParams& p, const int item)
             else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         }
         lds_barrier();
-        iteration(t, smem + ((t + NS - 1) % NS) * STAGE, smem + (t % NS) * STAGE);
-    }
+        iteration(tail, t, smem + ((t + NS - 1) % NS) * STAGE, smem + (t % NS) * STAGE);
+    };
+    for (int t = 0; t < ntiles - 1; ++t) step(std::false_type{}, t);
+    if (ntiles > 0) step(std::true_type{}, ntiles - 1);
 
     // ---- write the partial: S^T in C layout (column = feature 32nt + lq, row
     // d = 32dt + (r/4)*8 + 4h + r%4), z from the two lane halves; waves that
