@@ -25,6 +25,8 @@
 // fp32 kernel: the same map on the vector ALU in fp32.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "local_common.h"
 
 namespace rehyat {
@@ -197,31 +199,39 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
             uint16_t* ob = (uint16_t*)sd.out + bh * sd.out_bh_stride + (long long)(sd.r0 + row0) * 2 * D;
             const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)ob, (short)0, nrows * 2 * D * 2, 0x00020000);
+            // the wave's feature tile fixes the map (1 + elu for the first
+            // half of D', the square for the second): one instance each, so
+            // that no element carries a branch
+            auto layer2 = [&](auto square_c) {
+                constexpr bool SQUARE = decltype(square_c)::value;
+#pragma unroll 1
+                for (int rt = 0; rt < RB / 32; ++rt) {
+                    const int row = 32 * rt + lq;
+                    f32x16 acc = f32x16{};
 #pragma unroll
-            for (int rt = 0; rt < RB / 32; ++rt) {
-                const int row = 32 * rt + lq;
-                f32x16 acc = f32x16{};
-#pragma unroll
-                for (int s = 0; s < KS2; ++s) {
-                    const bf16x8 hf = lds_read_b128(hs, row * HID + (((2 * s + h) ^ hswz<CH>(row)) << 3));
-                    acc = mfma32x32x16(w2f[s], hf, acc);
-                }
-                // the next block's x into its slot before the first phi store:
-                // the compiler's wait for the x registers would otherwise
-                // include the stores issued after the loads
-                if (rt == 0 && b + 1 < b_end) store_x(xs + ((b + 1 - b_begin) & 1) * XT);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float y[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float ps = acc[4 * j + i] + b2v[4 * j + i];
-                        y[i] = wave < FT / 2 ? elu1(ps) : ps * ps;
+                    for (int s = 0; s < KS2; ++s) {
+                        const bf16x8 hf = lds_read_b128(hs, row * HID + (((2 * s + h) ^ hswz<CH>(row)) << 3));
+                        acc = mfma32x32x16(w2f[s], hf, acc);
                     }
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])}, ors,
-                                                          (row * 2 * D + 32 * wave + 8 * j + 4 * h) * 2, 0, 0);
+                    // the next block's x into its slot before the first phi store:
+                    // the compiler's wait for the x registers would otherwise
+                    // include the stores issued after the loads
+                    if (rt == 0 && b + 1 < b_end) store_x(xs + ((b + 1 - b_begin) & 1) * XT);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float ps = acc[4 * j + i] + b2v[4 * j + i];
+                            y[i] = SQUARE ? ps * ps : elu1(ps);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])},
+                                                              ors, (row * 2 * D + 32 * wave + 8 * j + 4 * h) * 2, 0, 0);
+                    }
                 }
-            }
+            };
+            if (wave < FT / 2) layer2(std::false_type{});
+            else layer2(std::true_type{});
         } else if (b + 1 < b_end) {
             store_x(xs + ((b + 1 - b_begin) & 1) * XT);
         }
