@@ -329,10 +329,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(BwdParams p) {
     // no masking needed; one instance each, so that neither has a branch inside)
     auto first_step = [&](int t, auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
-        // lane addressing re-derived per step behind an empty asm, so that the
-        // compiler does not keep every read's address live across the loop
+        // the first role's loop keeps its read addresses live across the loop
+        // (its own loop has the registers for them; the second role's does not)
         int ln = lane;
-        asm volatile("" : "+v"(ln));
         const int h = ln >> 5, lq = ln & 31;
         int toff[DT][2];
         {
