@@ -88,7 +88,8 @@ constexpr int kStateSubRowsBf16 = 1600;  // key rows per bf16 block-state workgr
 // only, so a streaming step that folds the same rows as a forward delta block
 // adds the same partials in the same order (the two results are bitwise
 // equal).  The bf16 size gives 3 workgroups per 3-frame block of 1560-token
-// frames, 216 workgroups for 12 heads and 6 blocks.
+// frames: 204 workgroups for 12 heads at 21 frames, T_c = 3, T_o = 1 (one
+// 2-frame block of 2 sub-blocks and five 3-frame blocks of 3).
 struct SubSplit {
     int n_sub, sub_rows;
 };
