@@ -31,6 +31,14 @@
 
 namespace rehyat {
 
+// Workgroup barrier after LDS writes that other waves read next: the barrier
+// alone does not wait for the writing wave's LDS operations, so they are
+// waited for first (s_waitcnt with lgkmcnt 0, vmcnt and expcnt at their maxima).
+__device__ __forceinline__ void lds_write_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+}
+
 namespace {
 
 constexpr int kMlpRows = 128;  // rows per block
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
         // this block's x is in its LDS slot (and every wave is done with the
         // hidden tile and with the x slot written next); the next block's x
         // goes to registers now, to LDS after layer 2
-        lds_barrier();
+        lds_write_barrier();
         if (b + 1 < b_end) fetch_x(b + 1);
         {
         const lds_u16* xcur = xs + ((b - b_begin) & 1) * XT;
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(kMlpRows * 4) void phi_mlp_bf16_kernel(MlpParams p)
             }
         }
         }
-        lds_barrier();
+        lds_write_barrier();  // every wave's hidden rows are in LDS
 
         // layer 2: psi^T rows [32 wave, +32), phi, store (a resource ending at
         // the side's last row drops the rows past it)
