@@ -34,7 +34,7 @@ namespace {
 // NINST) or of the V tile.  Virtual key row j < prev_rows reads the overlap
 // segment, the others read the clip at row j + seg_shift.  Rows past a
 // buffer's end read as zero.
-template <int NW, int OPW, int OPS, int NINST, int KTILE, int BN>
+template <int NW, int OPW, int OPS, int NINST, int KTILE, int BN, bool PLAIN>
 __device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile_idx, int prev_rows, int seg_shift,
                                                int rb, const int* op_row, const int* op_c16,
                                                __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
@@ -50,7 +50,7 @@ __device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile
             const int off_prev = j * rb + op_c16[o];
             const int off_clip = (j + seg_shift) * rb + op_c16[o];
             auto* lds = (__attribute__((address_space(3))) void*)dst;
-            if (prev_rows == 0) {  // whole-clip forward: one segment, scalar resource
+            if (PLAIN || prev_rows == 0) {  // whole-clip forward: one segment, scalar resource
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, lds, 16, off_clip, 0, 0, 0);
             } else if (isv) {
                 if (j < prev_rows) __builtin_amdgcn_raw_ptr_buffer_load_lds(vprs, lds, 16, off_prev, 0, 0, 0);
@@ -63,7 +63,9 @@ __device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile
     }
 }
 
-template <int D, int QB, int NW, int BN, int PHI, int LSTAGES>
+// PLAIN: a whole-clip launch that only stores out (no overlap segment, no lse,
+// fp32 copy or partials); its instance carries none of that code.
+template <int D, int QB, int NW, int BN, int PHI, int LSTAGES, bool PLAIN>
 __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     constexpr int C = D / 8;                     // 16-byte chunks per row
     constexpr int KTILE = BN * D;                // elements of one K (or V) tile
@@ -102,12 +104,13 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     const int q_start = f0 * p.HW + tile * BM;
     if (q_start >= q_end) return;
     const int w0 = max(f0 - p.To, 0) * p.HW;
-    const int nkeys = p.prev_rows + (q_end - w0);
+    const int prev_rows = PLAIN ? 0 : p.prev_rows;
+    const int nkeys = prev_rows + (q_end - w0);
 
     const uint16_t* qb_ptr = (const uint16_t*)p.q + bh * p.bh_stride;
     const uint16_t* kb_ptr = (const uint16_t*)p.k + bh * p.bh_stride;
     const uint16_t* vb_ptr = (const uint16_t*)p.v + bh * p.bh_stride;
-    const int seg_shift = w0 - p.prev_rows;     // virtual key j >= prev_rows is clip row j + seg_shift
+    const int seg_shift = w0 - prev_rows;     // virtual key j >= prev_rows is clip row j + seg_shift
     const uint16_t* kp_ptr = p.kp ? (const uint16_t*)p.kp + bh * p.prev_bh_stride : nullptr;
     const uint16_t* vp_ptr = p.vp ? (const uint16_t*)p.vp + bh * p.prev_bh_stride : nullptr;
 
@@ -131,9 +134,9 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vb_ptr), (short)0, q_end * rb, 0x00020000);
     const __amdgpu_buffer_rsrc_t kprs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kp_ptr ? kp_ptr : kb_ptr), (short)0, p.prev_rows * rb, 0x00020000);
+        (void*)(kp_ptr ? kp_ptr : kb_ptr), (short)0, prev_rows * rb, 0x00020000);
     const __amdgpu_buffer_rsrc_t vprs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vp_ptr ? vp_ptr : vb_ptr), (short)0, p.prev_rows * rb, 0x00020000);
+        (void*)(vp_ptr ? vp_ptr : vb_ptr), (short)0, prev_rows * rb, 0x00020000);
     int op_row[OPW], op_c16[OPW];
 #pragma unroll
     for (int o = 0; o < OPW; ++o) {
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
         op_c16[o] = ((pos % C) ^ swz<C>(pos / C)) * 16;
     }
     auto issue_tile = [&](int tile_idx, int stage) {
-        issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(smem + stage * STAGE, wave, tile_idx, p.prev_rows, seg_shift,
+        issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN, PLAIN>(smem + stage * STAGE, wave, tile_idx, prev_rows, seg_shift,
                                                        rb, op_row, op_c16, krs, vrs, kprs, vprs);
     };
 
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     const bool active = q_start + wave * QB * 32 < q_end;
     auto iteration = [&](auto tail, int it, lds_u16* __restrict__ fill, const lds_u16* __restrict__ cur) {
         if (it + PF < ntiles)
-            issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN>(fill, wave, it + PF, p.prev_rows, seg_shift, rb, op_row,
+            issue_tile_dma<NW, OPW, OPS, NINST, KTILE, BN, PLAIN>(fill, wave, it + PF, prev_rows, seg_shift, rb, op_row,
                                                            op_c16, krs, vrs, kprs, vprs);
         else if (STAGE_S && lin && it == ntiles - 1) {
             issue_state_dma<D, DP, NW>(fill, wave, lane, shi);
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(NW * 64) void local_bf16_kernel(LocalParams p) {
     if (!active) return;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-        finish_query_block<D, PHI>(p, qreg[qb], oacc[qb], msum[qb], m2[qb], mtrue[qb],
+        finish_query_block<D, PHI, PLAIN>(p, qreg[qb], oacc[qb], msum[qb], m2[qb], mtrue[qb],
                                    q_start + (wave * QB + qb) * 32 + lq, q_end, bh, t, h, lq, lin, s_lds,
                                    s_lds_lo);
 }
@@ -387,13 +390,19 @@ hipError_t launch_d(const LocalParams& p, hipStream_t s) {
     const int blocks = p.BH * p.n_chunks * p.tiles_per_chunk;
     if (blocks <= 0) return hipSuccess;
     dim3 grid(blocks), block(NW * 64);
+    const bool plain = p.prev_rows == 0 && p.lse == nullptr && p.out_f32 == nullptr && p.pm == nullptr &&
+                       p.pnt == nullptr && p.poS == nullptr && p.poL == nullptr && p.pnL == nullptr;
+#define REHYAT_LOCAL_LAUNCH(PHI_)                                                                    \
+    if (plain) local_bf16_kernel<D, QB, NW, BN, PHI_, kStages, true><<<grid, block, 0, s>>>(p);       \
+    else local_bf16_kernel<D, QB, NW, BN, PHI_, kStages, false><<<grid, block, 0, s>>>(p);
     switch (p.phi) {
-    case kPhiNone: local_bf16_kernel<D, QB, NW, BN, kPhiNone, kStages><<<grid, block, 0, s>>>(p); break;
-    case kPhiElu1: local_bf16_kernel<D, QB, NW, BN, kPhiElu1, kStages><<<grid, block, 0, s>>>(p); break;
-    case kPhiPoly2: local_bf16_kernel<D, QB, NW, BN, kPhiPoly2, kStages><<<grid, block, 0, s>>>(p); break;
-    case kPhiFeat: local_bf16_kernel<D, QB, NW, BN, kPhiFeat, kStages><<<grid, block, 0, s>>>(p); break;
+    case kPhiNone: REHYAT_LOCAL_LAUNCH(kPhiNone) break;
+    case kPhiElu1: REHYAT_LOCAL_LAUNCH(kPhiElu1) break;
+    case kPhiPoly2: REHYAT_LOCAL_LAUNCH(kPhiPoly2) break;
+    case kPhiFeat: REHYAT_LOCAL_LAUNCH(kPhiFeat) break;
     default: return hipErrorInvalidValue;
     }
+#undef REHYAT_LOCAL_LAUNCH
     return hipGetLastError();
 }
 

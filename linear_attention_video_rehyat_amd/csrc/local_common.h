@@ -70,7 +70,8 @@ __device__ __forceinline__ void issue_state_dma(lds_u16* dst, int wave, int lane
 //   y = (2^-M2' a^S + 2^-M2 a^L) / (2^-M2' n^S + 2^-M2 n^L),  M2 = max(m2, log2 n^L),
 // which equals (a^S + a^L)/(n^S + n^L) exactly and stays finite in fp32.
 // Writes y in bf16, or the per-branch partials when any partial buffer is set.
-template <int D, int PHI>
+// PLAIN: the launch only stores out (no lse, fp32 copy or partials).
+template <int D, int PHI, bool PLAIN = false>
 __device__ __forceinline__ void finish_query_block(const LocalParams& p, const bf16x8 (&q)[D / 16],
                                                    const f32x16 (&oacc)[D / 32], float msum, float m2,
                                                    float mtrue, int row, int q_end, int bh, int t, int h,
@@ -143,12 +144,12 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
     }
     const float den = cs * lsum + cl * nl;  // (n^S + n^L) 2^-M2
     const float inv = 1.0f / den;
-    const bool store_out =
-        p.pm == nullptr && p.poS == nullptr && p.poL == nullptr && p.pnt == nullptr && p.pnL == nullptr;
+    const bool store_out = PLAIN || (p.pm == nullptr && p.poS == nullptr && p.poL == nullptr &&
+                                     p.pnt == nullptr && p.pnL == nullptr);
     const bool valid = row < q_end;  // rows past the chunk end hold duplicated queries
     const long long prow = bh * (long long)(p.bh_stride / D) + row;
-    if (p.lse && valid && h == 0) p.lse[prow] = kLn2 * (M2 + __builtin_amdgcn_logf(den));
-    if (!store_out && valid && h == 0) {
+    if (!PLAIN && p.lse && valid && h == 0) p.lse[prow] = kLn2 * (M2 + __builtin_amdgcn_logf(den));
+    if (!PLAIN && !store_out && valid && h == 0) {
         if (p.pm) p.pm[prow] = mtrue;
         if (p.pnt) p.pnt[prow] = lsum * __builtin_amdgcn_exp2f(m2 - mtrue * kLog2e);
         if (p.pnL) p.pnL[prow] = nl;
@@ -227,10 +228,10 @@ __device__ __forceinline__ void finish_query_block(const LocalParams& p, const b
                 }
                 u32x2 w = {pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3])};
                 *(u32x2*)(ob_ptr + (long long)row * D + 32 * dt + 8 * g + 4 * h) = w;
-                if (p.out_f32)
+                if (!PLAIN && p.out_f32)
                     *(f32x4*)(p.out_f32 + prow * D + 32 * dt + 8 * g + 4 * h) = f32x4{y[0], y[1], y[2], y[3]};
             }
-        } else {
+        } else if constexpr (!PLAIN) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int col = 32 * dt + 8 * g + 4 * h;
