@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
 # it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "e79b85a6ce3dce52", "workload": "wan_21x30x52",
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "968c633e0fe2ba15", "workload": "wan_21x30x52",
                         "phi": "elu1", "chunk_frames": 3, "bytes": (276426.0 * 2.0 + 98306.0 * 1.0) * 1024}
 
 

@@ -39,28 +39,39 @@ __device__ __forceinline__ void issue_tile_dma(lds_u16* base, int wave, int tile
                                                int rb, const int* op_row, const int* op_c16,
                                                __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                                __amdgpu_buffer_rsrc_t kprs, __amdgpu_buffer_rsrc_t vprs) {
+    // SEG: 0 every row of the tile lies in the clip, 1 every row in the overlap
+    // segment, 2 the tile straddles the two (chosen row by row)
+    auto issue = [&](auto seg_c) {
+        constexpr int SEG = decltype(seg_c)::value;
 #pragma unroll
-    for (int o = 0; o < OPW; ++o) {
-        const int op = wave + o * NW;
-        if (OPS % NW == 0 || op < OPS) {
-            // K or V: decided at compile time when the ops split evenly over the waves
-            const bool isv = NINST % NW == 0 ? o >= NINST / NW : op >= NINST;
-            lds_u16* dst = base + (isv ? KTILE : 0) + 64 * (op % NINST) * 8;
-            const int j = tile_idx * BN + op_row[o];  // virtual key row
-            const int off_prev = j * rb + op_c16[o];
-            const int off_clip = (j + seg_shift) * rb + op_c16[o];
-            auto* lds = (__attribute__((address_space(3))) void*)dst;
-            if (PLAIN || prev_rows == 0) {  // whole-clip forward: one segment, scalar resource
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, lds, 16, off_clip, 0, 0, 0);
-            } else if (isv) {
-                if (j < prev_rows) __builtin_amdgcn_raw_ptr_buffer_load_lds(vprs, lds, 16, off_prev, 0, 0, 0);
-                else __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds, 16, off_clip, 0, 0, 0);
-            } else {
-                if (j < prev_rows) __builtin_amdgcn_raw_ptr_buffer_load_lds(kprs, lds, 16, off_prev, 0, 0, 0);
-                else __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds, 16, off_clip, 0, 0, 0);
+        for (int o = 0; o < OPW; ++o) {
+            const int op = wave + o * NW;
+            if (OPS % NW == 0 || op < OPS) {
+                // K or V: decided at compile time when the ops split evenly over the waves
+                const bool isv = NINST % NW == 0 ? o >= NINST / NW : op >= NINST;
+                lds_u16* dst = base + (isv ? KTILE : 0) + 64 * (op % NINST) * 8;
+                const int j = tile_idx * BN + op_row[o];  // virtual key row
+                const int off_prev = j * rb + op_c16[o];
+                const int off_clip = (j + seg_shift) * rb + op_c16[o];
+                auto* lds = (__attribute__((address_space(3))) void*)dst;
+                if (SEG == 0) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, lds, 16, off_clip, 0, 0, 0);
+                } else if (SEG == 1) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vprs : kprs, lds, 16, off_prev, 0, 0, 0);
+                } else if (isv) {
+                    if (j < prev_rows) __builtin_amdgcn_raw_ptr_buffer_load_lds(vprs, lds, 16, off_prev, 0, 0, 0);
+                    else __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds, 16, off_clip, 0, 0, 0);
+                } else {
+                    if (j < prev_rows) __builtin_amdgcn_raw_ptr_buffer_load_lds(kprs, lds, 16, off_prev, 0, 0, 0);
+                    else __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds, 16, off_clip, 0, 0, 0);
+                }
             }
         }
-    }
+    };
+    const int t0 = tile_idx * BN;  // first virtual key row of the tile (uniform)
+    if (PLAIN || t0 >= prev_rows) issue(std::integral_constant<int, 0>{});
+    else if (t0 + BN <= prev_rows) issue(std::integral_constant<int, 1>{});
+    else issue(std::integral_constant<int, 2>{});
 }
 
 // PLAIN: a whole-clip launch that only stores out (no overlap segment, no lse,
