@@ -17,8 +17,8 @@ Three independent forms of the same computation live here:
   from the §3.3 set definitions written in token units, ``W = exp(QK^T)*M_S +
   (phi(Q) phi(K)^T)*M_L``, ``Y = W V / rowsum(W)``.
 * :class:`RecurrentState` / :func:`recurrent` -- the chunk-wise RNN form the
-  paper derives (§3.3 and the abstract's "chunk-wise recurrent reformulation and
-  constant memory usage"): chunks in order, carrying the linear sums (S, z) of
+  paper derives (ReHyAt page, Abstract and §3.3: processed chunk by chunk, the
+  method's memory stays fixed as the video grows): chunks in order, carrying the linear sums (S, z) of
   §3.1 plus the keys/values of the last T_o frames (the next chunk's overlap).
 
 Readings where the text is silent are listed in ``rehyat_oracle.c``'s header;
