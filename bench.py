@@ -43,9 +43,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # HBM bytes per dispatch of the local-softmax kernel at the default workload, from
 # rocprofv3 FETCH_SIZE (x 2.0) + WRITE_SIZE (x 1.0), the factors a plain 1 GiB copy
 # gives (profiles/local_bf16_wan_21x30x52.md).  Valid only for the kernel source
-# it was measured on: reported as null once local_bf16.hip changes.
-LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "968c633e0fe2ba15", "workload": "wan_21x30x52",
-                        "phi": "elu1", "chunk_frames": 3, "bytes": (276426.0 * 2.0 + 98306.0 * 1.0) * 1024}
+# it was measured on: reported as null once local_bf16.hip or its flags change.
+LOCAL_KERNEL_TRAFFIC = {"source_sha256_16": "0f59890a5d110b3c", "workload": "wan_21x30x52",
+                        "phi": "elu1", "chunk_frames": 3, "bytes": (277098.6 * 2.0 + 98288.8 * 1.0) * 1024}
 
 
 LOCAL_KERNEL_SOURCES = ("local_bf16.hip", "local_common.h", "common.h")
@@ -66,6 +66,8 @@ def local_kernel_sha():
     start = text.index(b"struct LocalParams {")
     end = text.index(b"// Block-state pass:", start)
     h.update(text[start:end])
+    from linear_attention_video_rehyat_amd.build import file_flags  # the kernel's compile flags
+    h.update(repr(tuple(file_flags("local_bf16.hip"))).encode())
     return h.hexdigest()[:16]
 
 

@@ -40,6 +40,19 @@ COMMON_FLAGS = [
 ]
 
 
+# LLVM's iterative ILP scheduler for the kernels of the whole-clip forward: the
+# forward at the Wan2.1-1.3B shape (local, block-state and scan kernels) ran
+# 1.2 % faster than with the default scheduler, with bit-identical results
+# (interleaved timing in one process).  Other files keep the default.
+SCHED_ILP = ("-mllvm", "-amdgpu-sched-strategy=iterative-ilp")
+FILE_FLAGS = {"local_bf16.hip": SCHED_ILP, "state_bf16.hip": SCHED_ILP, "scan.hip": SCHED_ILP}
+
+
+def file_flags(name: str):
+    """Extra hipcc flags of one source file (by base name)."""
+    return FILE_FLAGS.get(name, ())
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
@@ -61,7 +74,7 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = {ex.submit(_compile, s, o): s for s, o in zip(srcs, objs)}
+        futs = {ex.submit(_compile, s, o, file_flags(os.path.basename(s))): s for s, o in zip(srcs, objs)}
         for f in cf.as_completed(futs):
             warn = f.result()
             if verbose and warn.strip():
